@@ -1,0 +1,169 @@
+/*
+ * dgw4 — W4A16 routed-expert (grouped MoE) layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every pointer argument named "device" is device memory owned by the
+ * caller; the library allocates nothing, keeps no state between calls and
+ * never synchronises the host: each call only enqueues kernels on `stream`
+ * (a hipStream_t passed as void*; NULL means the default stream) and returns.
+ * Results are ready when the stream reaches that point. Calls are therefore
+ * safe to capture in a HIP graph.
+ *
+ * Errors: every function returns a dgw4_status. Argument checks happen on the
+ * host before any HIP call; on an error nothing is launched and no output is
+ * written. DGW4_ERR_HIP reports a failed launch (hipGetLastError).
+ * Data-dependent preconditions (values inside device buffers) are not checked
+ * on the host; where a kernel meets an invalid value the behaviour is stated
+ * at the function, and no kernel reads or writes outside the buffers whose
+ * sizes are given here.
+ *
+ * Pages cited (by title and section):
+ *   [card]  "DiffusionGemma-26B-A4B W4A16" model card
+ *   [kcard] "dg-w4-kernels" kernel card
+ *   [blog]  "Inference: Making every denoising pass fast" (Part 2)
+ *
+ * Packed weight format ([card] "Checkpoint format", dg-w4a16-v1): asymmetric
+ * uint4, an fp16 scale s and fp16 zero point z per group of g consecutive
+ * weights along the contraction dimension K, two nibbles per byte with
+ * byte j of a row = q[2j] | q[2j+1] << 4. A weight is w = (q - z) * s.
+ * For a matrix of N rows (outputs) by K (contraction):
+ *   q  uint8  [N, K/2]   row-major
+ *   s  fp16   [N, K/g]   (passed as uint16 bit patterns)
+ *   z  fp16   [N, K/g]   (integer-valued)
+ * An expert stack adds a leading [E] dimension to each of the three.
+ * gate_up_proj of expert e is [2m, d]: rows 0..m-1 are the gate projection,
+ * rows m..2m-1 the up projection. down_proj is [d, m].
+ */
+#ifndef DGW4_H
+#define DGW4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define DGW4_API __attribute__((visibility("default")))
+#else
+#define DGW4_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DGW4_OK = 0,
+    DGW4_ERR_INVALID_ARG = 1,   /* null pointer, bad shape or size */
+    DGW4_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. g not in {64,128}) */
+    DGW4_ERR_WORKSPACE = 3,     /* workspace smaller than the queried size */
+    DGW4_ERR_HIP = 4            /* a kernel launch failed */
+} dgw4_status;
+
+/* Human-readable name of a status code (static storage). */
+DGW4_API const char *dgw4_status_string(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+DGW4_API int dgw4_version(void);
+
+/*
+ * dgw4_quantize_rtn — min/max round-to-nearest uint4 packer.
+ * ([kcard] "W4A16": quantize_w4(W, group_size); [card] "Benchmarks":
+ *  round-to-nearest min/max, no calibration; [blog] "The first constraint was
+ *  capacity": per-group integer codes, scale and zero point; groups of 128
+ *  for gate/up and 64 for down.)
+ *
+ * Per row and group G of g weights, in fp32 with IEEE round-to-nearest-even:
+ *   lo = min G, hi = max G
+ *   s  = fp16((hi - lo) / 15); s = 1 if that rounds to zero
+ *   z  = clamp(rint(-lo / s), -2048, 2048)
+ *   q  = clamp(rint(w / s) + z, 0, 15)
+ * Bit-exact and deterministic.
+ *
+ *   w       device fp32 [E, N, K], finite, (hi - lo)/15 <= 65504 per group
+ *   E, N, K E >= 1, N >= 1, K >= 2 even, K % g == 0
+ *   g       64 or 128 (others: DGW4_ERR_UNSUPPORTED)
+ *   q       device uint8 [E, N, K/2]        (output)
+ *   s, z    device uint16 [E, N, K/g]       (output, fp16 bits)
+ */
+DGW4_API int dgw4_quantize_rtn(const float *w, int E, int N, int K, int g,
+                      uint8_t *q, uint16_t *s, uint16_t *z, void *stream);
+
+/*
+ * dgw4_align_capacity — size of the padded assignment list for dgw4_align:
+ *   cap = T*topk + E*(block_m - 1); tile_expert holds cap / block_m entries.
+ * Returns 0 for invalid arguments.
+ */
+DGW4_API size_t dgw4_align_capacity(int T, int topk, int E, int block_m);
+
+/*
+ * dgw4_align — sync-free token-to-expert alignment.
+ * ([blog] "Quantisation alone leaves a sparse execution problem": sort the
+ *  assignments by expert and pad into regular blocks; [kcard] "Grouped MoE":
+ *  sync-free and graph safe; [blog] "The final best W4 MoE kernel": 32-row
+ *  blocks.)
+ *
+ * Flat assignment id i = t*topk + k, A = T*topk.
+ *   counts[e]      number of i with topk_ids[i] == e
+ *   offsets[e]     exclusive scan of ceil(counts/block_m)*block_m; offsets[E] = total
+ *   sorted_ids[p]  expert e's flat ids in ascending order at [offsets[e], ...);
+ *                  every other entry of [0, cap) holds A (pad)
+ *   tile_expert[j] expert of the block_m-row tile j < offsets[E]/block_m; -1 after
+ *   num_padded[0]  offsets[E]
+ * Every output entry is written, so the result does not depend on the
+ * buffers' previous contents. Bit-exact and deterministic.
+ *
+ *   topk_ids    device int32 [T, topk]; an id outside [0, E) is skipped (it
+ *               is counted nowhere and never written)
+ *   T >= 0, 1 <= topk, 1 <= E <= 1024, block_m in {16, 32, 64}
+ *   counts      device int32 [E]                         (output)
+ *   offsets     device int32 [E + 1]                     (output)
+ *   sorted_ids  device int32 [cap]                       (output)
+ *   tile_expert device int32 [cap / block_m]             (output)
+ *   num_padded  device int32 [1]                         (output)
+ */
+DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m,
+               int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+               int32_t *tile_expert, int32_t *num_padded, void *stream);
+
+/*
+ * dgw4_moe_forward — one routed-expert layer with W4A16 experts.
+ * ([kcard] "Grouped MoE": fused_moe_w4_v2(hidden, experts, topk_ids,
+ *  topk_weights) with packed gu_q/gu_s/gu_z and dn_q/dn_s/dn_z, one launch for
+ *  all experts, activation folded into the first GEMM's epilogue, fixed-order
+ *  combine; [blog] "Quantisation alone leaves a sparse execution problem":
+ *  each token runs through its routed experts, the outputs are weighted and
+ *  added in a fixed order; [card] "Checkpoint format": the packed layout.)
+ *
+ * For every token t:
+ *   out[t] = sum over k = 0..topk-1 (ascending) of
+ *            w[t,k] * down_e( gelu_tanh(gate_e(x[t])) * up_e(x[t] ) ),  e = ids[t,k]
+ * with expert weights dequantised as w = (q - z) * s. Accumulation is fp32;
+ * the gated intermediate is rounded to fp16 once, each expert output is kept
+ * in fp32 and the combine sums in ascending k in fp32 without atomics, then
+ * rounds once to fp16. Repeated calls on the same inputs give bit-identical
+ * results.
+ *
+ *   x          device fp16 bits [T, d]
+ *   topk_ids   device int32 [T, topk]; ids outside [0, E) contribute nothing
+ *   topk_w     device fp32 [T, topk]
+ *   T >= 0, 1 <= topk <= E, 1 <= E <= 1024
+ *   d, m       d % gu_g == 0, m % dn_g == 0 (so both are multiples of 64)
+ *   gu_q/s/z   device, gate_up stack [E, 2m, d] packed with group gu_g
+ *   dn_q/s/z   device, down stack [E, d, m] packed with group dn_g
+ *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED)
+ *   workspace  device scratch of at least *ws_bytes bytes, 256-byte aligned.
+ *              If workspace is NULL, the required size is written to
+ *              *ws_bytes and nothing is launched. Contents on entry are
+ *              irrelevant; the call overwrites what it uses.
+ *   ws_bytes   host pointer: in = size of workspace, out (query) = required
+ *   out        device fp16 bits [T, d]                   (output)
+ */
+DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                     int T, int topk, int E, int d, int m,
+                     const uint8_t *gu_q, const uint16_t *gu_s, const uint16_t *gu_z, int gu_g,
+                     const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
+                     void *workspace, size_t *ws_bytes, uint16_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGW4_H */

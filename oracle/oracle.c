@@ -129,7 +129,8 @@ void orc_f16_to_f32_array(const uint16_t *src, long n, float *dst)
  *   lo, hi = min, max of the group          (fp32, exact)
  *   s      = fp16_rn((hi - lo) / 15)         (fp32 subtract and divide)
  *   s      = 1 if s rounds to zero           (degenerate group)
- *   z      = clamp(rint(-lo / s), -2048, 2048)          (integer, stored fp16)
+ *   z      = clamp(rint(-lo / s), -2048, 2048)          (integer, stored fp16;
+ *            a zero point of 0 is stored as +0)
  *   q_i    = clamp(rint(w_i / s) + z, 0, 15)            (integer add after rint)
  *
  * rint is round-half-to-even. Nibble packing ([card] "Checkpoint format"):
@@ -166,8 +167,9 @@ int orc_quantize_rtn(const float *w, int E, int N, int K, int g,
             float zf = rintf(-lo / sf);
             if (zf < -2048.0f) zf = -2048.0f;
             if (zf > 2048.0f) zf = 2048.0f;
+            const int zi = (int)zf;                  /* an integer: zero has no sign */
             s[r * ng + gi] = sb;
-            z[r * ng + gi] = orc_f32_to_f16(zf);     /* exact: integer, |zf| <= 2048 */
+            z[r * ng + gi] = orc_f32_to_f16((float)zi);   /* exact: |zi| <= 2048 */
             for (int i = 0; i < g; ++i) {
                 float v = rintf(wg[i] / sf) + zf;
                 if (v < 0.0f) v = 0.0f;

@@ -1,0 +1,94 @@
+"""The C ABI (include/dgw4.h) on the host: the library loads, exports every
+declared function, and rejects bad arguments before any HIP call. No kernel
+is launched here."""
+import ctypes
+
+import pytest
+
+import w4a16_grouped_moe_amd as dg
+from w4a16_grouped_moe_amd import binding as B
+
+
+def test_exports_every_declared_function():
+    names = B.header_functions()
+    assert set(names) >= {"dgw4_quantize_rtn", "dgw4_align", "dgw4_moe_forward",
+                          "dgw4_align_capacity", "dgw4_status_string", "dgw4_version"}
+    L = dg.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert dg.status_string(0) == "DGW4_OK"
+    assert dg.status_string(3) == "DGW4_ERR_WORKSPACE"
+    assert dg.status_string(99) == "DGW4_UNKNOWN_STATUS"
+    assert dg.version() >= 100
+
+
+def test_align_capacity():
+    assert dg.align_capacity(256, 8, 128, 32) == 256 * 8 + 128 * 31
+    assert dg.align_capacity(0, 8, 128, 32) == 128 * 31
+    assert dg.align_capacity(-1, 8, 128, 32) == 0
+
+
+def test_workspace_query():
+    n = dg.workspace_bytes(256, 8, 128, 2816, 704)
+    cap = 256 * 8 + 128 * 31
+    # H fp16 [cap, m] + Y fp32 [A, d] + alignment buffers
+    assert n >= cap * 704 * 2 + 2048 * 2816 * 4
+    assert n < cap * 704 * 2 + 2048 * 2816 * 4 + 64 * 1024
+    assert n % 256 == 0
+
+
+def _fwd(**kw):
+    a = dict(x=1 << 12, ids=1 << 12, w=1 << 12, T=4, topk=2, E=8, d=512, m=192,
+             gq=1 << 12, gs=1 << 12, gz=1 << 12, gg=128, dq=1 << 12, ds=1 << 12, dz=1 << 12,
+             dg=64, ws=1 << 12, out=1 << 12, n=1 << 30)
+    a.update(kw)
+    n = ctypes.c_size_t(a["n"])
+    return dg.lib().dgw4_moe_forward(a["x"], a["ids"], a["w"], a["T"], a["topk"], a["E"],
+                                     a["d"], a["m"], a["gq"], a["gs"], a["gz"], a["gg"],
+                                     a["dq"], a["ds"], a["dz"], a["dg"], a["ws"],
+                                     ctypes.byref(n), a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gq=None), B.ERR_INVALID_ARG),
+    (dict(x=None), B.ERR_INVALID_ARG),
+    (dict(topk=9), B.ERR_INVALID_ARG),           # topk > E
+    (dict(E=0), B.ERR_INVALID_ARG),
+    (dict(E=2000, topk=2), B.ERR_INVALID_ARG),   # > 1024 experts
+    (dict(d=500), B.ERR_INVALID_ARG),            # d % 128
+    (dict(m=100), B.ERR_INVALID_ARG),            # m % 64
+    (dict(gg=32), B.ERR_UNSUPPORTED),
+    (dict(dg=96), B.ERR_UNSUPPORTED),
+    (dict(ws=(1 << 12) + 4), B.ERR_INVALID_ARG),  # misaligned workspace
+    (dict(x=(1 << 12) + 2), B.ERR_INVALID_ARG),   # misaligned x
+    (dict(n=16), B.ERR_WORKSPACE),
+    (dict(T=-1), B.ERR_INVALID_ARG),
+])
+def test_forward_rejects(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_forward_t0_is_noop():
+    assert _fwd(T=0, x=None, ids=None, w=None, out=None) == B.OK
+
+
+def test_quantize_rejects():
+    q = dg.lib().dgw4_quantize_rtn
+    assert q(None, 1, 1, 128, 128, 1 << 12, 1 << 12, 1 << 12, None) == B.ERR_INVALID_ARG
+    assert q(1 << 12, 1, 1, 127, 64, 1 << 12, 1 << 12, 1 << 12, None) == B.ERR_INVALID_ARG
+    assert q(1 << 12, 1, 1, 192, 128, 1 << 12, 1 << 12, 1 << 12, None) == B.ERR_INVALID_ARG
+    assert q(1 << 12, 1, 1, 96, 32, 1 << 12, 1 << 12, 1 << 12, None) == B.ERR_UNSUPPORTED
+    assert q(1 << 12, 0, 1, 128, 64, 1 << 12, 1 << 12, 1 << 12, None) == B.ERR_INVALID_ARG
+
+
+def test_align_rejects():
+    a = dg.lib().dgw4_align
+    p = 1 << 12
+    assert a(p, 4, 2, 8, 24, p, p, p, p, p, None) == B.ERR_INVALID_ARG    # block_m
+    assert a(p, 4, 2, 1025, 32, p, p, p, p, p, None) == B.ERR_INVALID_ARG
+    assert a(None, 4, 2, 8, 32, p, p, p, p, p, None) == B.ERR_INVALID_ARG
+    assert a(p, 4, 2, 8, 32, p, None, p, p, p, None) == B.ERR_INVALID_ARG
+    assert a(p, -1, 2, 8, 32, p, p, p, p, p, None) == B.ERR_INVALID_ARG

@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer work (packing, alignment) is compared bit for bit; the layer output
+element by element within max|err| <= 1e-2 * max|ref|, on the tiny workload
+in full, on shapes with several tiles and ragged tails in full, and on the
+full-size workloads at sampled tokens in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4a16_grouped_moe_amd as dg
+from synth import CONFIGS, routing
+from tests import layer_cases as lc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm device")
+    dg.lib()
+
+
+# ------------------------------------------------------------- quantiser ----
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_quantize_edge_groups(g):
+    lc.log(f"[quant] edge groups g={g}")
+    rng = np.random.default_rng(g)
+    rows = []
+    rows.append(np.zeros(4 * g, np.float32))                                # all zero
+    rows.append(np.full(4 * g, 0.75, np.float32))                           # constant
+    r = np.zeros(4 * g, np.float32); r[1:g] = np.linspace(0.01, 1, g - 1); rows.append(r)  # min +0
+    r = -np.zeros(4 * g, np.float32); r[g:] = rng.standard_normal(3 * g); rows.append(r)   # -0s
+    rows.append((1000 + np.arange(4 * g) * 1e-3).astype(np.float32))       # saturated z
+    rows.append((rng.standard_normal(4 * g) * 1e-6).astype(np.float32))    # subnormal-ish s
+    rows.append((rng.standard_t(2, 4 * g) * 1e-2).astype(np.float32))      # outliers
+    rows.append(rng.uniform(0.5, 2, 4 * g).astype(np.float32))             # one-signed
+    rows.append(-rng.uniform(0.5, 2, 4 * g).astype(np.float32))
+    base = np.zeros(4 * g, np.int64) + 5
+    base[0], base[1] = 0, 15
+    r = ((base - 5) * 0.0625).astype(np.float32); r[2:6] = np.array([0.5, 1.5, -0.5, 2.5]) * 0.0625
+    rows.append(r)                                                          # exact ties
+    w = np.stack(rows)[None]
+    lc.pack_both(w, g)
+
+
+@pytest.mark.parametrize("name", ["tiny", "full"])
+def test_quantize_workload_bitexact(name):
+    shp = CONFIGS[name]
+    lc.log(f"[quant] workload {name}")
+    from synth import expert_weights
+    gw, dw = expert_weights(shp)
+    lc.pack_both(gw, shp.g_gu)
+    lc.pack_both(dw, shp.g_dn)
+
+
+# ------------------------------------------------------------- alignment ----
+
+def _align_case(ids, E, bm):
+    ref = oracle.align(ids, E, bm)
+    # garbage in the output buffers must not matter
+    got = dg.align(torch.from_numpy(ids).cuda(), E, bm)
+    torch.cuda.synchronize()
+    for k in ref:
+        assert np.array_equal(got[k].cpu().numpy(), ref[k]), k
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_align_random(bm):
+    lc.log(f"[align] random bm={bm}")
+    rng = np.random.default_rng(bm)
+    for T, topk, E in [(1, 1, 1), (7, 3, 5), (64, 2, 8), (256, 8, 128), (1024, 8, 128),
+                       (333, 4, 1024), (5, 8, 8)]:
+        _align_case(rng.integers(0, E, (T, topk)).astype(np.int32), E, bm)
+
+
+@pytest.mark.parametrize("name", ["tiny", "full", "skew", "wide"])
+def test_align_workloads(name):
+    shp = CONFIGS[name]
+    lc.log(f"[align] workload {name}")
+    ids, _ = routing(shp)
+    _align_case(ids, shp.E, 32)
+
+
+def test_align_degenerate():
+    lc.log("[align] degenerate")
+    _align_case(np.zeros((300, 8), np.int32), 128, 32)                 # one expert takes all
+    _align_case(np.full((3, 2), 7, np.int32), 8, 16)
+    _align_case(np.zeros((0, 8), np.int32), 128, 32)                    # no tokens
+
+
+def test_align_skips_out_of_range_ids():
+    lc.log("[align] out-of-range ids")
+    ids = np.array([[0, 9], [-1, 3], [3, 3]], np.int32)
+    got = dg.align(torch.from_numpy(ids).cuda(), 8, 16)
+    torch.cuda.synchronize()
+    assert list(got["counts"].cpu().numpy()) == [1, 0, 0, 3, 0, 0, 0, 0]
+    sid = got["sorted_ids"].cpu().numpy()
+    assert list(sid[:1]) == [0] and list(sid[16:19]) == [3, 4, 5]
+
+
+# --------------------------------------------------------------- forward ----
+
+def test_forward_tiny_every_element():
+    L = lc.build(CONFIGS["tiny"])
+    lc.assert_close(lc.gpu_forward(L), lc.oracle_forward(L), "tiny")
+
+
+@pytest.mark.parametrize("case", [
+    # several 32-row tiles per expert with a ragged last tile; ragged last K chunk
+    dict(name="ragged", E=8, topk=2, T=333, d=640, m=320),
+    # down N-blocks with idle waves (576 = 4.5 x 128), g=64 for gate_up too
+    dict(name="edge_n", E=6, topk=3, T=97, d=576, m=192, g_gu=64),
+    # g=128 on the down projection, single expert, top-1
+    dict(name="top1", E=1, topk=1, T=45, d=256, m=256, g_dn=128),
+    # one token
+    dict(name="one_token", E=16, topk=4, T=1, d=512, m=192),
+])
+def test_forward_shapes_every_element(case):
+    shp = lc.custom_shape(**case)
+    L = lc.build(shp)
+    lc.assert_close(lc.gpu_forward(L), lc.oracle_forward(L), case["name"])
+
+
+def test_forward_duplicate_and_dropped_ids():
+    shp = lc.custom_shape("dups", E=8, topk=4, T=40, d=512, m=192)
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, 8, (40, 4)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]                                   # duplicates are independent
+    w = rng.uniform(0.1, 1, (40, 4)).astype(np.float32)
+    bad = ids.copy()
+    bad[::3, 2] = -1                                        # dropped by the GPU path
+    bad[1::5, 3] = 8
+    L = lc.build(shp, ids=bad, w=w)
+    gpu = lc.gpu_forward(L)
+    keep = (bad >= 0) & (bad < 8)
+    L.ids = np.where(keep, bad, 0).astype(np.int32)         # oracle: same layer without them
+    L.w = np.where(keep, w, 0).astype(np.float32)
+    lc.assert_close(gpu, lc.oracle_forward(L), "dups/dropped")
+
+
+def _sampled(L, n, seed, what):
+    gpu = lc.gpu_forward(L)
+    rng = np.random.default_rng(seed)
+    toks = np.sort(rng.choice(L.shape.T, n, replace=False)).astype(np.int32)
+    ref = lc.oracle_forward(L, tokens=toks)
+    lc.assert_close(gpu[toks], ref, what)
+    return gpu
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    return lc.build(CONFIGS["full"])
+
+
+def test_forward_full_sampled(full_layer):
+    _sampled(full_layer, 24, 1, "full(sampled 24 tokens)")
+
+
+def test_forward_full_deterministic_100(full_layer):
+    L = full_layer
+    ws = torch.empty(dg.workspace_bytes(L.shape.T, L.shape.topk, L.shape.E, L.shape.d,
+                                        L.shape.m), dtype=torch.uint8, device="cuda")
+    first = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=ws).clone()
+    bad = 0
+    for i in range(100):
+        if i % 10 == 0:                          # stale workspace contents must not matter
+            ws.random_(0, 256)
+        o = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=ws)
+        bad += int(not torch.equal(o.view(torch.int16), first.view(torch.int16)))
+    torch.cuda.synchronize()
+    lc.log(f"[determinism] 100 runs, {bad} differing")
+    assert bad == 0
+
+
+def test_forward_skew_sampled():
+    L = lc.build(CONFIGS["skew"])
+    _sampled(L, 16, 2, "skew(sampled 16 tokens)")
+
+
+def test_forward_wide_sampled():
+    L = lc.build(CONFIGS["wide"])
+    _sampled(L, 16, 3, "wide(sampled 16 tokens)")

@@ -137,6 +137,13 @@ def test_degenerate_groups():
     assert np.array_equal(d[0, 0], np.zeros(2 * g))               # all-zero row exact
     assert np.all(np.abs(d - w) <= 0.5)
     assert np.array_equal(d[0, 2, g:], np.full(g, -3.0))          # integer constant exact
+    # the zero point is an integer: a zero point of 0 is stored as +0, also
+    # when the group minimum is +0.0 (so -lo/s is -0.0)
+    assert np.all(z[0, 0] == 0x0000)
+    w2 = np.zeros((1, 1, g), np.float32)
+    w2[0, 0, 1:] = np.linspace(0.01, 1.0, g - 1, dtype=np.float32)
+    _, _, z2 = oracle.quantize_rtn(w2, g)
+    assert z2[0, 0, 0] == 0x0000
 
 
 def test_saturated_zero_point():

@@ -1,0 +1,18 @@
+"""dgw4: W4A16 routed-expert (grouped MoE) layer for AMD Instinct MI355X.
+
+The compute lives in libdgw4.so (hand-written HIP for gfx950, C ABI in
+include/dgw4.h); this package only binds it for torch device tensors.
+"""
+from .binding import (  # noqa: F401
+    BLOCK_M,
+    Dgw4Error,
+    align,
+    align_capacity,
+    header_functions,
+    lib,
+    moe_forward,
+    quantize_rtn,
+    status_string,
+    version,
+    workspace_bytes,
+)

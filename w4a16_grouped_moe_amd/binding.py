@@ -1,0 +1,191 @@
+"""Python binding of libdgw4 (include/dgw4.h): argument marshalling only.
+
+Functions take torch tensors that live on a ROCm device, check dtypes,
+shapes and contiguity, and pass raw device pointers plus the current HIP
+stream to the C ABI. Every step of the layer runs in the library's HIP
+kernels; there is no fallback: if the library is missing or a call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdgw4.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dgw4.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+BLOCK_M = 32          # rows per tile used inside dgw4_moe_forward
+
+_lib = None
+
+
+class Dgw4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status_string(status)}")
+        self.status = status
+
+
+def lib():
+    """Load libdgw4.so (built in-tree). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m w4a16_grouped_moe_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.dgw4_status_string.restype = ctypes.c_char_p
+        L.dgw4_status_string.argtypes = [I]
+        L.dgw4_version.restype = I
+        L.dgw4_version.argtypes = []
+        L.dgw4_quantize_rtn.restype = I
+        L.dgw4_quantize_rtn.argtypes = [P, I, I, I, I, P, P, P, P]
+        L.dgw4_align_capacity.restype = S
+        L.dgw4_align_capacity.argtypes = [I, I, I, I]
+        L.dgw4_align.restype = I
+        L.dgw4_align.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
+        L.dgw4_moe_forward.restype = I
+        L.dgw4_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
+                                       P, P, P, I, P, P, P, I,
+                                       P, ctypes.POINTER(S), P, P]
+        _lib = L
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/dgw4.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"DGW4_API\s+[\w\s\*]*?\b(dgw4_\w+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().dgw4_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().dgw4_version()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise Dgw4Error(fn, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+_F16 = (torch.float16, torch.int16, torch.uint16)
+
+
+def quantize_rtn(w: torch.Tensor, g: int):
+    """w fp32 [..., N, K] (device) -> (q uint8 [..., N, K/2], s fp16 [..., N, K/g],
+    z fp16 [..., N, K/g])."""
+    pw = _dev(w, "w", (torch.float32,))
+    *lead, N, K = w.shape
+    E = 1
+    for v in lead:
+        E *= v
+    q = torch.empty((*lead, N, K // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((*lead, N, K // g), dtype=torch.float16, device=w.device)
+    z = torch.empty((*lead, N, K // g), dtype=torch.float16, device=w.device)
+    _check("dgw4_quantize_rtn", lib().dgw4_quantize_rtn(
+        pw, E, N, K, g, q.data_ptr(), s.data_ptr(), z.data_ptr(), _stream(w)))
+    return q, s, z
+
+
+def align_capacity(T: int, topk: int, E: int, block_m: int) -> int:
+    return int(lib().dgw4_align_capacity(T, topk, E, block_m))
+
+
+def align(topk_ids: torch.Tensor, E: int, block_m: int = BLOCK_M) -> dict:
+    """topk_ids int32 [T, topk] (device) -> dict of device int32 tensors
+    counts [E], offsets [E+1], sorted_ids [cap], tile_expert [cap/block_m],
+    num_padded [1]."""
+    pid = _dev(topk_ids, "topk_ids", (torch.int32,))
+    T, topk = topk_ids.shape
+    cap = align_capacity(T, topk, E, block_m)
+    if cap == 0:
+        raise ValueError("invalid alignment shape")
+    dev = topk_ids.device
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sorted_ids=torch.empty(cap, dtype=torch.int32, device=dev),
+               tile_expert=torch.empty(cap // block_m, dtype=torch.int32, device=dev),
+               num_padded=torch.empty(1, dtype=torch.int32, device=dev))
+    _check("dgw4_align", lib().dgw4_align(
+        pid, T, topk, E, block_m, out["counts"].data_ptr(), out["offsets"].data_ptr(),
+        out["sorted_ids"].data_ptr(), out["tile_expert"].data_ptr(),
+        out["num_padded"].data_ptr(), _stream(topk_ids)))
+    return out
+
+
+def workspace_bytes(T: int, topk: int, E: int, d: int, m: int, gu_g: int = 128,
+                    dn_g: int = 64) -> int:
+    """Device workspace dgw4_moe_forward needs for this shape (host-only query)."""
+    n = ctypes.c_size_t(0)
+    _check("dgw4_moe_forward(query)", lib().dgw4_moe_forward(
+        None, None, None, T, topk, E, d, m, None, None, None, gu_g, None, None, None, dn_g,
+        None, ctypes.byref(n), None, None))
+    return int(n.value)
+
+
+def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
+                gu: tuple, dn: tuple, workspace: torch.Tensor | None = None,
+                out: torch.Tensor | None = None) -> torch.Tensor:
+    """One routed-expert layer.
+
+    x fp16 [T, d]; topk_ids int32 [T, topk]; topk_w fp32 [T, topk];
+    gu = (q uint8 [E, 2m, d/2], s fp16 [E, 2m, d/g], z fp16 [E, 2m, d/g], g);
+    dn = (q uint8 [E, d, m/2], s, z, g). Returns out fp16 [T, d].
+    ``workspace`` (uint8 device tensor of at least workspace_bytes(...)) is
+    allocated here when not given; pass one to avoid allocation per call."""
+    gq, gs, gz, gg = gu
+    dq, ds, dz, dg = dn
+    T, d = x.shape
+    topk = topk_ids.shape[1]
+    E = gq.shape[0]
+    m = dq.shape[2] * 2
+    if gq.shape != (E, 2 * m, d // 2) or dq.shape != (E, d, m // 2):
+        raise ValueError(f"packed shapes {tuple(gq.shape)} / {tuple(dq.shape)} do not match "
+                         f"x {tuple(x.shape)}")
+    if gs.shape != (E, 2 * m, d // gg) or gz.shape != gs.shape:
+        raise ValueError("gate_up scale/zero shape mismatch")
+    if ds.shape != (E, d, m // dg) or dz.shape != ds.shape:
+        raise ValueError("down scale/zero shape mismatch")
+    if topk_ids.shape != (T, topk) or topk_w.shape != (T, topk):
+        raise ValueError("topk_ids / topk_weights must be [T, topk]")
+    ptrs = [_dev(x, "x", _F16), _dev(topk_ids, "topk_ids", (torch.int32,)),
+            _dev(topk_w, "topk_w", (torch.float32,)),
+            _dev(gq, "gu_q", (torch.uint8,)), _dev(gs, "gu_s", _F16), _dev(gz, "gu_z", _F16),
+            _dev(dq, "dn_q", (torch.uint8,)), _dev(ds, "dn_s", _F16), _dev(dz, "dn_z", _F16)]
+    need = workspace_bytes(T, topk, E, d, m, gg, dg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    pws = _dev(workspace, "workspace", (torch.uint8,))
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float16, device=x.device)
+    pout = _dev(out, "out", _F16)
+    n = ctypes.c_size_t(workspace.numel())
+    _check("dgw4_moe_forward", lib().dgw4_moe_forward(
+        ptrs[0], ptrs[1], ptrs[2], T, topk, E, d, m,
+        ptrs[3], ptrs[4], ptrs[5], gg, ptrs[6], ptrs[7], ptrs[8], dg,
+        pws, ctypes.byref(n), pout, _stream(x)))
+    return out

@@ -1,0 +1,64 @@
+// Fixed-order, atomic-free weighted combine.
+//
+// Follows the Part 2 blog, "Quantisation alone leaves a sparse execution
+// problem" (each token's eight expert outputs are reduced in a fixed order,
+// never with index_add_ or atomics, because a change in the last bit can flip
+// a denoising acceptance decision), and the model card's "What's in here"
+// (fixed-order reduction instead of index_add_).
+//
+// out[t, c] = fp16( sum_{k = 0..topk-1, ascending} w[t, k] * Y[t*topk + k, c] )
+// in fp32, skipping k whose expert id is outside [0, E). Each thread owns four
+// neighbouring columns of one token: 16-byte loads of Y, one 8-byte store.
+// Every output element is produced by exactly one thread with a fixed
+// sequence of operations, so the result is bitwise reproducible.
+#include "dgw4_internal.hpp"
+
+#pragma clang fp contract(off)
+
+namespace dgw4 {
+namespace {
+
+__global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__ y,
+                                                      const int32_t *__restrict__ ids,
+                                                      const float *__restrict__ w, int topk,
+                                                      int E, int d4, uint2 *__restrict__ out)
+{
+    const int t = blockIdx.y;
+    const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c4 >= d4)
+        return;
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    for (int k = 0; k < topk; ++k) {
+        const int e = ids[(size_t)t * topk + k];
+        if (e < 0 || e >= E)
+            continue;
+        const float wk = w[(size_t)t * topk + k];
+        const float4 v = y[((size_t)t * topk + k) * d4 + c4];
+        a0 = __fadd_rn(a0, __fmul_rn(wk, v.x));
+        a1 = __fadd_rn(a1, __fmul_rn(wk, v.y));
+        a2 = __fadd_rn(a2, __fmul_rn(wk, v.z));
+        a3 = __fadd_rn(a3, __fmul_rn(wk, v.w));
+    }
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);   // RN-even
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)a2);
+    const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)a3);
+    out[(size_t)t * d4 + c4] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *y, const int32_t *topk_ids, const float *topk_w,
+                          int T, int topk, int E, int d, uint16_t *out, hipStream_t stream)
+{
+    if (T == 0)
+        return hipSuccess;
+    const int d4 = d / 4;
+    const dim3 grid((d4 + 255) / 256, T);
+    combine_kernel<<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const float4 *>(y), topk_ids,
+                                                   topk_w, topk, E, d4,
+                                                   reinterpret_cast<uint2 *>(out));
+    return hipGetLastError();
+}
+
+}  // namespace dgw4

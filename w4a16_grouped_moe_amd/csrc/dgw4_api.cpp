@@ -1,0 +1,196 @@
+// C-ABI entry points of libdgw4 (declared in include/dgw4.h).
+//
+// Host side only: argument validation, workspace layout and the launch
+// sequence. No allocation, no host synchronisation, no state between calls.
+#include "dgw4.h"
+
+#include "dgw4_internal.hpp"
+
+#include <limits.h>
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool group_supported(int g) { return g == 64 || g == 128; }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? DGW4_OK : DGW4_ERR_HIP; }
+
+// Workspace of one forward call: alignment buffers, the gated intermediate H
+// (fp16, one row per padded assignment) and the per-assignment expert
+// outputs Y (fp32, one row per flat assignment id).
+struct Layout {
+    size_t counts, offsets, num_padded, tile_expert, sorted_ids, h, y, total;
+};
+
+Layout layout(long long A, int E, int d, int m, long long cap)
+{
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = round_up(off + bytes);
+        return at;
+    };
+    L.counts = take(sizeof(int32_t) * (size_t)E);
+    L.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+    L.num_padded = take(sizeof(int32_t));
+    L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
+    L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
+    L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
+    L.y = take(sizeof(float) * (size_t)A * (size_t)d);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dgw4_status_string(int status)
+{
+    switch (status) {
+    case DGW4_OK: return "DGW4_OK";
+    case DGW4_ERR_INVALID_ARG: return "DGW4_ERR_INVALID_ARG";
+    case DGW4_ERR_UNSUPPORTED: return "DGW4_ERR_UNSUPPORTED";
+    case DGW4_ERR_WORKSPACE: return "DGW4_ERR_WORKSPACE";
+    case DGW4_ERR_HIP: return "DGW4_ERR_HIP";
+    default: return "DGW4_UNKNOWN_STATUS";
+    }
+}
+
+int dgw4_version(void) { return 100; }   // 0.1.0
+
+int dgw4_quantize_rtn(const float *w, int E, int N, int K, int g, uint8_t *q, uint16_t *s,
+                      uint16_t *z, void *stream)
+{
+    if (!w || !q || !s || !z)
+        return DGW4_ERR_INVALID_ARG;
+    if (E < 1 || N < 1 || K < 2 || (K % 2) != 0 || g < 1)
+        return DGW4_ERR_INVALID_ARG;
+    if (!group_supported(g))
+        return DGW4_ERR_UNSUPPORTED;
+    if (K % g != 0 || !aligned(w, 8))
+        return DGW4_ERR_INVALID_ARG;
+    const long long groups = (long long)E * N * (K / g);
+    return from_hip(dgw4::launch_quantize_rtn(w, groups, g, q, s, z, (hipStream_t)stream));
+}
+
+size_t dgw4_align_capacity(int T, int topk, int E, int block_m)
+{
+    if (T < 0 || topk < 1 || E < 1 || block_m < 1)
+        return 0;
+    const long long cap = (long long)T * topk + (long long)E * (block_m - 1);
+    return cap > INT_MAX ? 0 : (size_t)cap;
+}
+
+int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int32_t *counts,
+               int32_t *offsets, int32_t *sorted_ids, int32_t *tile_expert, int32_t *num_padded,
+               void *stream)
+{
+    if (T < 0 || topk < 1 || E < 1 || E > dgw4::kMaxExperts)
+        return DGW4_ERR_INVALID_ARG;
+    if (block_m != 16 && block_m != 32 && block_m != 64)
+        return DGW4_ERR_INVALID_ARG;
+    if ((T > 0 && !topk_ids) || !counts || !offsets || !sorted_ids || !tile_expert || !num_padded)
+        return DGW4_ERR_INVALID_ARG;
+    const size_t cap = dgw4_align_capacity(T, topk, E, block_m);
+    if (cap == 0)
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_align(topk_ids, T * topk, E, block_m, (long long)cap, counts,
+                                       offsets, sorted_ids, tile_expert, num_padded,
+                                       (hipStream_t)stream));
+}
+
+int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w, int T,
+                     int topk, int E, int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
+                     const uint16_t *gu_z, int gu_g, const uint8_t *dn_q, const uint16_t *dn_s,
+                     const uint16_t *dn_z, int dn_g, void *workspace, size_t *ws_bytes,
+                     uint16_t *out, void *stream)
+{
+    if (!ws_bytes)
+        return DGW4_ERR_INVALID_ARG;
+    if (T < 0 || E < 1 || E > dgw4::kMaxExperts || topk < 1 || topk > E || d < 1 || m < 1)
+        return DGW4_ERR_INVALID_ARG;
+    if (gu_g < 1 || dn_g < 1)
+        return DGW4_ERR_INVALID_ARG;
+    if (!group_supported(gu_g) || !group_supported(dn_g))
+        return DGW4_ERR_UNSUPPORTED;
+    if (d % gu_g != 0 || m % dn_g != 0)
+        return DGW4_ERR_INVALID_ARG;
+    const long long A = (long long)T * topk;
+    const size_t cap = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
+    if (cap == 0 || A > INT_MAX)
+        return DGW4_ERR_INVALID_ARG;
+    const Layout L = layout(A, E, d, m, (long long)cap);
+    if (!workspace) {
+        *ws_bytes = L.total;
+        return DGW4_OK;
+    }
+    if (!gu_q || !gu_s || !gu_z || !dn_q || !dn_s || !dn_z)
+        return DGW4_ERR_INVALID_ARG;
+    if (T > 0 && (!x || !topk_ids || !topk_w || !out))
+        return DGW4_ERR_INVALID_ARG;
+    if (!aligned(workspace, kAlign) || !aligned(x, 16) || !aligned(gu_q, 16) ||
+        !aligned(dn_q, 16) || !aligned(out, 8))
+        return DGW4_ERR_INVALID_ARG;
+    if (*ws_bytes < L.total)
+        return DGW4_ERR_WORKSPACE;
+    if (T == 0)
+        return DGW4_OK;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *ws = static_cast<char *>(workspace);
+    int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
+    int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
+    int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
+    int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
+    uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
+    float *y = reinterpret_cast<float *>(ws + L.y);
+
+    hipError_t err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap,
+                                        counts, offsets, sorted_ids, tile_expert, num_padded, st);
+    if (err != hipSuccess)
+        return DGW4_ERR_HIP;
+
+    dgw4::GemmArgs g{};
+    g.sorted_ids = sorted_ids;
+    g.tile_expert = tile_expert;
+    g.counts = counts;
+    g.offsets = offsets;
+    g.num_padded = num_padded;
+    g.topk = topk;
+    g.A = (int)A;
+    g.max_tiles = (int)(cap / dgw4::kBlockM);
+
+    g.a_src = x;
+    g.q = gu_q;
+    g.s = gu_s;
+    g.z = gu_z;
+    g.K = d;
+    g.n_w = 2 * m;
+    g.n_out = m;
+    g.out = h;
+    if ((err = dgw4::launch_gate_up(g, gu_g, st)) != hipSuccess)
+        return DGW4_ERR_HIP;
+
+    g.a_src = h;
+    g.q = dn_q;
+    g.s = dn_s;
+    g.z = dn_z;
+    g.K = m;
+    g.n_w = d;
+    g.n_out = d;
+    g.out = y;
+    if ((err = dgw4::launch_down(g, dn_g, st)) != hipSuccess)
+        return DGW4_ERR_HIP;
+
+    return from_hip(dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st));
+}
+
+}  // extern "C"

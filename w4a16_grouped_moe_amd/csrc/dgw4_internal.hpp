@@ -1,0 +1,51 @@
+// Internal declarations shared by the dgw4 HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dgw4 {
+
+// Rows of the padded assignment list handled by one GEMM workgroup
+// (two 16-row MFMA blocks).
+constexpr int kBlockM = 32;
+
+// Largest expert count the single-workgroup alignment kernel supports.
+constexpr int kMaxExperts = 1024;
+
+// Launchers: plain enqueue on `stream`, no host synchronisation. Shapes are
+// validated by the C-ABI layer before these are called.
+hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t *q,
+                               uint16_t *s, uint16_t *z, hipStream_t stream);
+
+hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
+                        int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+                        int32_t *tile_expert, int32_t *num_padded, hipStream_t stream);
+
+struct GemmArgs {
+    const uint16_t *a_src;      // gate_up: x [T, d]; down: H [cap, m]
+    const int32_t *sorted_ids;  // [cap]
+    const int32_t *tile_expert; // [cap / kBlockM]
+    const int32_t *counts;      // [E]
+    const int32_t *offsets;     // [E + 1]
+    const int32_t *num_padded;  // [1]
+    const uint8_t *q;           // packed weights [E, n_w, K/2]
+    const uint16_t *s;          // [E, n_w, K/g]
+    const uint16_t *z;          // [E, n_w, K/g]
+    int K;                      // contraction width (d for gate_up, m for down)
+    int n_w;                    // weight rows per expert (2m or d)
+    int n_out;                  // output columns (m or d)
+    int topk;
+    int A;                      // T * topk; also the pad sentinel in sorted_ids
+    int max_tiles;              // cap / kBlockM
+    void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp32 [A, d]
+};
+
+hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
+hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
+
+hipError_t launch_combine(const float *y, const int32_t *topk_ids, const float *topk_w,
+                          int T, int topk, int E, int d, uint16_t *out, hipStream_t stream);
+
+}  // namespace dgw4
