@@ -162,6 +162,25 @@ DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const 
                      const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
                      void *workspace, size_t *ws_bytes, uint16_t *out, void *stream);
 
+/*
+ * dgw4_moe_forward_timed — dgw4_moe_forward with stage events, for per-kernel
+ * timing of the same launch sequence (same kernels, same arguments, same
+ * results). events is an array of n_events = 5 caller-created hipEvent_t
+ * handles (passed as void*); they are recorded on `stream` before the
+ * alignment kernel and after each of the four kernels (align, gate_up, down,
+ * combine). Elapsed time between consecutive events is the duration of one
+ * stage. events == NULL behaves exactly like dgw4_moe_forward; any other
+ * n_events is DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL)
+ * records nothing.
+ */
+DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
+                                    const float *topk_w, int T, int topk, int E, int d, int m,
+                                    const uint8_t *gu_q, const uint16_t *gu_s,
+                                    const uint16_t *gu_z, int gu_g, const uint8_t *dn_q,
+                                    const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
+                                    void *workspace, size_t *ws_bytes, uint16_t *out,
+                                    void *stream, void *const *events, int n_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -53,6 +53,11 @@ def lib():
         L.dgw4_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                        P, P, P, I, P, P, P, I,
                                        P, ctypes.POINTER(S), P, P]
+        L.dgw4_moe_forward_timed.restype = I
+        L.dgw4_moe_forward_timed.argtypes = [P, P, P, I, I, I, I, I,
+                                             P, P, P, I, P, P, P, I,
+                                             P, ctypes.POINTER(S), P, P,
+                                             ctypes.POINTER(P), I]
         _lib = L
     return _lib
 
@@ -147,16 +152,22 @@ def workspace_bytes(T: int, topk: int, E: int, d: int, m: int, gu_g: int = 128,
     return int(n.value)
 
 
+STAGES = ("align", "gate_up", "down", "combine")
+
+
 def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
                 gu: tuple, dn: tuple, workspace: torch.Tensor | None = None,
-                out: torch.Tensor | None = None) -> torch.Tensor:
+                out: torch.Tensor | None = None, events=None) -> torch.Tensor:
     """One routed-expert layer.
 
     x fp16 [T, d]; topk_ids int32 [T, topk]; topk_w fp32 [T, topk];
     gu = (q uint8 [E, 2m, d/2], s fp16 [E, 2m, d/g], z fp16 [E, 2m, d/g], g);
     dn = (q uint8 [E, d, m/2], s, z, g). Returns out fp16 [T, d].
     ``workspace`` (uint8 device tensor of at least workspace_bytes(...)) is
-    allocated here when not given; pass one to avoid allocation per call."""
+    allocated here when not given; pass one to avoid allocation per call.
+    ``events``: optional list of 5 torch.cuda.Event(enable_timing=True),
+    recorded on the current stream before the alignment kernel and after each
+    of the four kernels (see STAGES)."""
     gq, gs, gz, gg = gu
     dq, ds, dz, dg = dn
     T, d = x.shape
@@ -184,8 +195,20 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
         out = torch.empty((T, d), dtype=torch.float16, device=x.device)
     pout = _dev(out, "out", _F16)
     n = ctypes.c_size_t(workspace.numel())
-    _check("dgw4_moe_forward", lib().dgw4_moe_forward(
-        ptrs[0], ptrs[1], ptrs[2], T, topk, E, d, m,
-        ptrs[3], ptrs[4], ptrs[5], gg, ptrs[6], ptrs[7], ptrs[8], dg,
-        pws, ctypes.byref(n), pout, _stream(x)))
+    if events is None:
+        _check("dgw4_moe_forward", lib().dgw4_moe_forward(
+            ptrs[0], ptrs[1], ptrs[2], T, topk, E, d, m,
+            ptrs[3], ptrs[4], ptrs[5], gg, ptrs[6], ptrs[7], ptrs[8], dg,
+            pws, ctypes.byref(n), pout, _stream(x)))
+    else:
+        if len(events) != 5:
+            raise ValueError("events: need 5 torch.cuda.Event")
+        for e in events:
+            if not e.cuda_event:          # torch creates the HIP event on first record
+                e.record()
+        ev = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
+        _check("dgw4_moe_forward_timed", lib().dgw4_moe_forward_timed(
+            ptrs[0], ptrs[1], ptrs[2], T, topk, E, d, m,
+            ptrs[3], ptrs[4], ptrs[5], gg, ptrs[6], ptrs[7], ptrs[8], dg,
+            pws, ctypes.byref(n), pout, _stream(x), ev, 5))
     return out

@@ -106,12 +106,19 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
                                        (hipStream_t)stream));
 }
 
-int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w, int T,
-                     int topk, int E, int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
-                     const uint16_t *gu_z, int gu_g, const uint8_t *dn_q, const uint16_t *dn_s,
-                     const uint16_t *dn_z, int dn_g, void *workspace, size_t *ws_bytes,
-                     uint16_t *out, void *stream)
+int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                           int T, int topk, int E, int d, int m, const uint8_t *gu_q,
+                           const uint16_t *gu_s, const uint16_t *gu_z, int gu_g,
+                           const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
+                           int dn_g, void *workspace, size_t *ws_bytes, uint16_t *out,
+                           void *stream, void *const *events, int n_events)
 {
+    if (events && n_events != 5)
+        return DGW4_ERR_INVALID_ARG;
+    if (events)
+        for (int i = 0; i < 5; ++i)
+            if (!events[i])
+                return DGW4_ERR_INVALID_ARG;
     if (!ws_bytes)
         return DGW4_ERR_INVALID_ARG;
     if (T < 0 || E < 1 || E > dgw4::kMaxExperts || topk < 1 || topk > E || d < 1 || m < 1)
@@ -144,6 +151,9 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
         return DGW4_OK;
 
     hipStream_t st = (hipStream_t)stream;
+    auto mark = [&](int i) {
+        return events ? hipEventRecord((hipEvent_t)events[i], st) : hipSuccess;
+    };
     char *ws = static_cast<char *>(workspace);
     int32_t *counts = reinterpret_cast<int32_t *>(ws + L.counts);
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
@@ -153,8 +163,12 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     float *y = reinterpret_cast<float *>(ws + L.y);
 
-    hipError_t err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap,
-                                        counts, offsets, sorted_ids, tile_expert, num_padded, st);
+    hipError_t err = mark(0);
+    if (err == hipSuccess)
+        err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
+                                 offsets, sorted_ids, tile_expert, num_padded, st);
+    if (err == hipSuccess)
+        err = mark(1);
     if (err != hipSuccess)
         return DGW4_ERR_HIP;
 
@@ -176,7 +190,7 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
     g.n_w = 2 * m;
     g.n_out = m;
     g.out = h;
-    if ((err = dgw4::launch_gate_up(g, gu_g, st)) != hipSuccess)
+    if ((err = dgw4::launch_gate_up(g, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
         return DGW4_ERR_HIP;
 
     g.a_src = h;
@@ -187,10 +201,24 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
     g.n_w = d;
     g.n_out = d;
     g.out = y;
-    if ((err = dgw4::launch_down(g, dn_g, st)) != hipSuccess)
+    if ((err = dgw4::launch_down(g, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
         return DGW4_ERR_HIP;
 
-    return from_hip(dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st));
+    if ((err = dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st)) != hipSuccess ||
+        (err = mark(4)) != hipSuccess)
+        return DGW4_ERR_HIP;
+    return DGW4_OK;
+}
+
+int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w, int T,
+                     int topk, int E, int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
+                     const uint16_t *gu_z, int gu_g, const uint8_t *dn_q, const uint16_t *dn_s,
+                     const uint16_t *dn_z, int dn_g, void *workspace, size_t *ws_bytes,
+                     uint16_t *out, void *stream)
+{
+    return dgw4_moe_forward_timed(x, topk_ids, topk_w, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g,
+                                  dn_q, dn_s, dn_z, dn_g, workspace, ws_bytes, out, stream,
+                                  nullptr, 0);
 }
 
 }  // extern "C"
