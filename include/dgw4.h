@@ -63,6 +63,10 @@ DGW4_API const char *dgw4_status_string(int status);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 DGW4_API int dgw4_version(void);
 
+/* Text of the HIP error behind the calling thread's most recent
+ * DGW4_ERR_HIP (static storage), or "no HIP error". */
+DGW4_API const char *dgw4_last_error(void);
+
 /*
  * dgw4_quantize_rtn — min/max round-to-nearest uint4 packer.
  * ([kcard] "W4A16": quantize_w4(W, group_size); [card] "Benchmarks":

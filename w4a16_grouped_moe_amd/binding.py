@@ -26,7 +26,10 @@ _lib = None
 
 class Dgw4Error(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn} returned {status_string(status)}")
+        msg = f"{fn} returned {status_string(status)}"
+        if status == ERR_HIP:
+            msg += f" ({lib().dgw4_last_error().decode()})"
+        super().__init__(msg)
         self.status = status
 
 
@@ -43,6 +46,8 @@ def lib():
         L.dgw4_status_string.argtypes = [I]
         L.dgw4_version.restype = I
         L.dgw4_version.argtypes = []
+        L.dgw4_last_error.restype = ctypes.c_char_p
+        L.dgw4_last_error.argtypes = []
         L.dgw4_quantize_rtn.restype = I
         L.dgw4_quantize_rtn.argtypes = [P, I, I, I, I, P, P, P, P]
         L.dgw4_align_capacity.restype = S

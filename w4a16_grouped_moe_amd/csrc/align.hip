@@ -1,72 +1,71 @@
-// Sync-free token-to-expert alignment.
+// Sync-free token-to-expert alignment, plus the forward's activation prep.
 //
 // Follows the Part 2 blog, "Quantisation alone leaves a sparse execution
 // problem" (sort assignments by expert, pad into regular blocks) and "The
 // final best W4 MoE kernel" (32-row blocks), and the "dg-w4-kernels" card,
 // "Grouped MoE" (alignment without host synchronisation).
 //
-// One workgroup of 512 threads does the whole job in four phases:
-//   1. histogram of expert ids in LDS (integer atomics: order-free result);
+// Workgroup 0 (1024 threads = 16 waves) aligns, with the ids held in LDS:
+//   1. histogram of expert ids with LDS integer atomics (order-free result);
 //   2. exclusive scan of the block-padded counts over experts (wave scans
 //      combined through LDS) -> offsets;
-//   3. stable scatter: assignments are taken 512 at a time in ascending flat
-//      order; inside a wave, lanes holding the same expert find each other
-//      with one ballot per id bit, which gives each lane its rank among
-//      earlier lanes; per-wave counts are turned into per-wave starting
-//      points by a pass over the 8 waves in order; a running cursor per expert
-//      carries across rounds. The result is the ascending-flat-id order
-//      inside every expert, independent of timing;
-//   4. pad entries and the tile -> expert map, each found by a binary search
-//      over the offsets.
+//   3. stable scatter in rounds of 1024 ids taken in ascending flat order:
+//      inside a wave, lanes holding the same expert find each other with one
+//      ballot per id bit, which gives each lane its rank among earlier lanes;
+//      one thread per expert turns the 16 per-wave counts into per-wave
+//      starting points (in wave order) and carries a running cursor across
+//      rounds. The result is the ascending-flat-id order inside every expert,
+//      independent of timing;
+//   4. each expert writes its own pad entries and tile map entries; the tail
+//      of the buffers past the total is filled by all threads.
 // Ids outside [0, E) are skipped everywhere.
+//
+// Workgroups 1.. (forward only) copy x into the permuted K order the GEMM
+// kernels consume (each 8 fp16 values reordered as [0,4,1,5,2,6,3,7]).
 #include "dgw4_internal.hpp"
 
 namespace dgw4 {
 namespace {
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
-__device__ inline int wave_inclusive_scan(int v, int lane)
+// 8 consecutive fp16 values -> the same values in order [0,4,1,5,2,6,3,7].
+__device__ inline uint4 permute8(uint4 v)
 {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int u = __shfl_up(v, off, 64);
-        if (lane >= off)
-            v += u;
-    }
-    return v;
+    uint4 o;
+    o.x = (v.x & 0xFFFFu) | (v.z << 16);
+    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    o.z = (v.y & 0xFFFFu) | (v.w << 16);
+    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return o;
 }
 
-// Largest e in [0, E) with offs[e] <= p (offs is non-decreasing, offs[0] = 0).
-__device__ inline int find_expert(const int *offs, int E, int p)
-{
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (offs[mid] <= p)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
+template <bool IDS_IN_LDS>
 __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restrict__ ids, int A,
-                                                        int E, int bm, long long cap,
+                                                        int E, int bm, int cap,
                                                         int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets,
                                                         int32_t *__restrict__ sorted_ids,
                                                         int32_t *__restrict__ tile_expert,
-                                                        int32_t *__restrict__ num_padded)
+                                                        int32_t *__restrict__ num_padded,
+                                                        const uint4 *__restrict__ x,
+                                                        uint4 *__restrict__ xp, long long x_segs)
 {
-    __shared__ int s_cnt[kMaxExperts];
-    __shared__ int s_off[kMaxExperts + 1];
-    __shared__ int s_cur[kMaxExperts];
-    __shared__ int s_wave[kWaves][kMaxExperts];
-    __shared__ int s_wsum[kWaves];
-
     const int tid = threadIdx.x;
+    if (blockIdx.x > 0) {
+        const long long stride = (long long)(gridDim.x - 1) * kThreads;
+        for (long long i = (long long)(blockIdx.x - 1) * kThreads + tid; i < x_segs; i += stride)
+            xp[i] = permute8(x[i]);
+        return;
+    }
+
+    extern __shared__ int32_t s_ids[];          // [A] when IDS_IN_LDS
+    __shared__ int32_t s_wave[kWaves][kMaxExperts];   // per-round, per-wave counts / starts
+    __shared__ int32_t s_cnt[kMaxExperts];
+    __shared__ int32_t s_cur[kMaxExperts];
+    __shared__ int32_t s_off[kMaxExperts + 1];
+    __shared__ int32_t s_wsum[kWaves];
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
@@ -77,50 +76,57 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
         for (int w = 0; w < kWaves; ++w)
             s_wave[w][e] = 0;
     }
+    if constexpr (IDS_IN_LDS) {
+        for (int i = tid; i < A; i += kThreads)
+            s_ids[i] = ids[i];
+    }
     __syncthreads();
+    auto id_at = [&](int i) { return IDS_IN_LDS ? s_ids[i] : ids[i]; };
 
     // 1. histogram
     for (int i = tid; i < A; i += kThreads) {
-        const int e = ids[i];
+        const int e = id_at(i);
         if (e >= 0 && e < E)
             atomicAdd(&s_cnt[e], 1);
     }
     __syncthreads();
 
-    // 2. exclusive scan of padded counts; thread tid owns experts 2tid, 2tid+1
-    const int e0 = 2 * tid, e1 = 2 * tid + 1;
-    const int p0 = e0 < E ? (s_cnt[e0] + bm - 1) / bm * bm : 0;
-    const int p1 = e1 < E ? (s_cnt[e1] + bm - 1) / bm * bm : 0;
-    const int incl = wave_inclusive_scan(p0 + p1, lane);
+    // 2. exclusive scan of padded counts (E <= 1024: one expert per thread)
+    const int padded = tid < E ? (s_cnt[tid] + bm - 1) / bm * bm : 0;
+    int incl = padded;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(incl, off, 64);
+        if (lane >= off)
+            incl += u;
+    }
     if (lane == 63)
         s_wsum[wave] = incl;
     __syncthreads();
     int base = 0;
     for (int w = 0; w < wave; ++w)
         base += s_wsum[w];
-    const int excl = base + incl - (p0 + p1);
-    if (e0 < E)
-        s_off[e0] = excl;
-    if (e1 < E)
-        s_off[e1] = excl + p0;
+    if (tid < E)
+        s_off[tid] = base + incl - padded;
     if (tid == kThreads - 1)
-        s_off[E] = base + incl;             // last thread's inclusive total
+        s_off[E] = base + incl;                 // total over all experts
     __syncthreads();
-    for (int e = tid; e < E; e += kThreads) {
-        counts[e] = s_cnt[e];
-        offsets[e] = s_off[e];
+    const int total = s_off[E];
+    if (tid < E) {
+        counts[tid] = s_cnt[tid];
+        offsets[tid] = s_off[tid];
     }
     if (tid == 0) {
-        offsets[E] = s_off[E];
-        num_padded[0] = s_off[E];
+        offsets[E] = total;
+        num_padded[0] = total;
     }
 
-    // 3. stable scatter
+    // 3. stable scatter, 1024 ids per round
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int base_i = 0; base_i < A; base_i += kThreads) {
         const int i = base_i + tid;
-        const int e = i < A ? ids[i] : -1;
+        const int e = i < A ? id_at(i) : -1;
         const bool valid = e >= 0 && e < E;
         unsigned long long mask = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
@@ -147,37 +153,69 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
         if (valid) {
             sorted_ids[s_off[e] + s_wave[wave][e] + rank] = i;
             if (rank == 0)
-                s_wave[wave][e] = 0;        // read by every lane of this wave above
+                s_wave[wave][e] = 0;            // read by every lane of this wave above
         }
+        // the next round's first LDS writes (the leaders above) only touch
+        // this wave's own row; the expert pass reads all rows after a barrier
     }
 
-    // 4. pads and tile map (disjoint from the positions written above)
-    const int total = s_off[E];
-    for (long long p = tid; p < cap; p += kThreads) {
-        bool pad = true;
-        if (p < total) {
-            const int e = find_expert(s_off, E, (int)p);
-            pad = (int)p - s_off[e] >= s_cnt[e];
-        }
-        if (pad)
+    // 4. pads and tile map: per expert, then the tail past the total
+    for (int e = tid; e < E; e += kThreads) {
+        for (int p = s_off[e] + s_cnt[e]; p < s_off[e + 1]; ++p)
             sorted_ids[p] = A;
+        for (int t = s_off[e] / bm; t < s_off[e + 1] / bm; ++t)
+            tile_expert[t] = e;
     }
-    const long long tiles = cap / bm;
-    for (long long j = tid; j < tiles; j += kThreads) {
-        const long long p = j * bm;
-        tile_expert[j] = p < total ? find_expert(s_off, E, (int)p) : -1;
-    }
+    for (int p = total + tid; p < cap; p += kThreads)
+        sorted_ids[p] = A;
+    for (int t = total / bm + tid; t < cap / bm; t += kThreads)
+        tile_expert[t] = -1;
 }
 
 }  // namespace
+
+// Largest assignment count whose ids are staged in LDS (64 KB).
+constexpr int kMaxIdsInLds = 16384;
 
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, hipStream_t stream)
 {
-    align_kernel<<<dim3(1), dim3(kThreads), 0, stream>>>(topk_ids, A, E, block_m, cap, counts,
-                                                          offsets, sorted_ids, tile_expert,
-                                                          num_padded);
+    return launch_prep(topk_ids, A, E, block_m, cap, counts, offsets, sorted_ids, tile_expert,
+                       num_padded, nullptr, nullptr, 0, stream);
+}
+
+hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
+                       int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+                       int32_t *tile_expert, int32_t *num_padded, const uint16_t *x,
+                       uint16_t *xp, long long x_elems, hipStream_t stream)
+{
+    const long long segs = x_elems / 8;
+    const long long want = (segs + kThreads - 1) / kThreads;
+    const int extra = (int)(want < 256 ? want : 256);
+    const dim3 grid(1 + extra);
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(x);
+    uint4 *xp4 = reinterpret_cast<uint4 *>(xp);
+    if (A <= kMaxIdsInLds) {
+        auto kern = align_kernel<true>;
+        const size_t lds = sizeof(int32_t) * (size_t)A;
+        static size_t lds_allowed = 64 * 1024;
+        if (lds > lds_allowed) {
+            hipError_t err = hipFuncSetAttribute((const void *)kern,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+            if (err != hipSuccess)
+                return err;
+            lds_allowed = lds;
+        }
+        kern<<<grid, dim3(kThreads), lds, stream>>>(topk_ids, A, E, block_m, (int)cap, counts,
+                                                    offsets, sorted_ids, tile_expert, num_padded,
+                                                    x4, xp4, segs);
+    } else {
+        align_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(
+            topk_ids, A, E, block_m, (int)cap, counts, offsets, sorted_ids, tile_expert,
+            num_padded, x4, xp4, segs);
+    }
     return hipGetLastError();
 }
 

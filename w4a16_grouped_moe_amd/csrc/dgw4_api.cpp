@@ -11,6 +11,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+// LDS of one CU; a GEMM workgroup must fit in half of it so that two can run.
+constexpr size_t kMaxGemmLds = 80 * 1024;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -18,16 +20,24 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool group_supported(int g) { return g == 64 || g == 128; }
 
-int from_hip(hipError_t e) { return e == hipSuccess ? DGW4_OK : DGW4_ERR_HIP; }
+thread_local hipError_t g_last_hip = hipSuccess;   // last failed HIP call of this thread
 
-// Workspace of one forward call: alignment buffers, the gated intermediate H
-// (fp16, one row per padded assignment) and the per-assignment expert
-// outputs Y (fp32, one row per flat assignment id).
+int from_hip(hipError_t e)
+{
+    if (e == hipSuccess)
+        return DGW4_OK;
+    g_last_hip = e;
+    return DGW4_ERR_HIP;
+}
+
+// Workspace of one forward call: alignment buffers, x in the GEMM's K order,
+// the gated intermediate H (fp16, one row per padded assignment) and the
+// per-assignment expert outputs Y (fp32, one row per flat assignment id).
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, sorted_ids, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, sorted_ids, xp, h, y, total;
 };
 
-Layout layout(long long A, int E, int d, int m, long long cap)
+Layout layout(long long A, int T, int E, int d, int m, long long cap)
 {
     Layout L{};
     size_t off = 0;
@@ -41,6 +51,7 @@ Layout layout(long long A, int E, int d, int m, long long cap)
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
+    L.xp = take(sizeof(uint16_t) * (size_t)T * (size_t)d);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take(sizeof(float) * (size_t)A * (size_t)d);
     L.total = off;
@@ -64,6 +75,11 @@ const char *dgw4_status_string(int status)
 }
 
 int dgw4_version(void) { return 100; }   // 0.1.0
+
+const char *dgw4_last_error(void)
+{
+    return g_last_hip == hipSuccess ? "no HIP error" : hipGetErrorString(g_last_hip);
+}
 
 int dgw4_quantize_rtn(const float *w, int E, int N, int K, int g, uint8_t *q, uint16_t *s,
                       uint16_t *z, void *stream)
@@ -133,7 +149,14 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     const size_t cap = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
     if (cap == 0 || A > INT_MAX)
         return DGW4_ERR_INVALID_ARG;
-    const Layout L = layout(A, E, d, m, (long long)cap);
+    if (dgw4::gemm_lds_bytes(true, d, gu_g) > kMaxGemmLds ||
+        dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds)
+        return DGW4_ERR_UNSUPPORTED;
+    // the GEMMs address x, H and one expert's packed weights with 32-bit offsets
+    if ((long long)T * d * 2 >= (1LL << 31) || (long long)cap * m * 2 >= (1LL << 31) ||
+        (long long)2 * m * d / 2 >= (1LL << 31))
+        return DGW4_ERR_UNSUPPORTED;
+    const Layout L = layout(A, T, E, d, m, (long long)cap);
     if (!workspace) {
         *ws_bytes = L.total;
         return DGW4_OK;
@@ -160,17 +183,19 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
+    uint16_t *xp = reinterpret_cast<uint16_t *>(ws + L.xp);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     float *y = reinterpret_cast<float *>(ws + L.y);
 
     hipError_t err = mark(0);
     if (err == hipSuccess)
-        err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
-                                 offsets, sorted_ids, tile_expert, num_padded, st);
+        err = dgw4::launch_prep(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
+                                offsets, sorted_ids, tile_expert, num_padded, x, xp,
+                                (long long)T * d, st);
     if (err == hipSuccess)
         err = mark(1);
     if (err != hipSuccess)
-        return DGW4_ERR_HIP;
+        return from_hip(err);
 
     dgw4::GemmArgs g{};
     g.sorted_ids = sorted_ids;
@@ -182,7 +207,8 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     g.A = (int)A;
     g.max_tiles = (int)(cap / dgw4::kBlockM);
 
-    g.a_src = x;
+    g.a_src = xp;
+    g.a_rows = T;
     g.q = gu_q;
     g.s = gu_s;
     g.z = gu_z;
@@ -191,9 +217,10 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     g.n_out = m;
     g.out = h;
     if ((err = dgw4::launch_gate_up(g, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
-        return DGW4_ERR_HIP;
+        return from_hip(err);
 
     g.a_src = h;
+    g.a_rows = (int)cap;
     g.q = dn_q;
     g.s = dn_s;
     g.z = dn_z;
@@ -202,11 +229,11 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     g.n_out = d;
     g.out = y;
     if ((err = dgw4::launch_down(g, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
-        return DGW4_ERR_HIP;
+        return from_hip(err);
 
     if ((err = dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st)) != hipSuccess ||
         (err = mark(4)) != hipSuccess)
-        return DGW4_ERR_HIP;
+        return from_hip(err);
     return DGW4_OK;
 }
 

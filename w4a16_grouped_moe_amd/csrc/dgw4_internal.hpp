@@ -23,8 +23,19 @@ hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, hipStream_t stream);
 
+// The alignment plus, in extra workgroups of the same launch, a copy of x
+// [x_elems fp16] into xp with each 8 values in the GEMM's K order.
+hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
+                       int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
+                       int32_t *tile_expert, int32_t *num_padded, const uint16_t *x,
+                       uint16_t *xp, long long x_elems, hipStream_t stream);
+
+// LDS one GEMM workgroup needs for contraction width K and group size g.
+size_t gemm_lds_bytes(bool gated, int K, int g);
+
 struct GemmArgs {
-    const uint16_t *a_src;      // gate_up: x [T, d]; down: H [cap, m]
+    const uint16_t *a_src;      // gate_up: x [T, d]; down: H [cap, m] (both permuted per 8)
+    int a_rows;                 // rows of a_src (T or cap)
     const int32_t *sorted_ids;  // [cap]
     const int32_t *tile_expert; // [cap / kBlockM]
     const int32_t *counts;      // [E]

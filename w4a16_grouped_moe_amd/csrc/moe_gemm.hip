@@ -6,47 +6,52 @@
 // "W4A16" (the GEMM reads packed nibbles and dequantises inline); the model
 // card, "Checkpoint format" (w = (q - z) * s, one scale/zero per group along
 // K, byte j = q[2j] | q[2j+1] << 4; the group size matches the K step so one
-// scale and zero load serves a whole K chunk); and the Part 2 blog,
-// "Quantisation alone leaves a sparse execution problem" and "The final best
-// W4 MoE kernel" (assignments sorted by expert and padded to 32-row blocks).
+// scale and zero serve a whole K chunk); and the Part 2 blog, "Quantisation
+// alone leaves a sparse execution problem" and "The final best W4 MoE
+// kernel" (assignments sorted by expert and padded to 32-row blocks).
 //
 // gfx950 design
 // -------------
 // Grid (N-block, tile): tile = one 32-row block of the padded assignment list
-// (one expert), N-block = 4 waves x 2 MFMA column tiles of 16 weight rows.
+// (one expert), N-block = WAVES waves x 2 MFMA column tiles of 16 weight rows.
 // Tiles past the device-side total exit at once, so the grid is static and
 // the host never reads the routing.
 //
 // Each wave streams its 32 weight rows once, straight from the canonical
-// packed layout: per group and column tile a lane loads g/8 bytes (a 16-byte
-// dwordx4 for g=128, 8 bytes for g=64) of one weight row; the four lane
-// groups of 16 cover one whole group of that row. Loads run D groups ahead in
-// registers and stay in flight across the workgroup barriers.
+// packed layout: per group and column tile a lane loads g/8 bytes (16 bytes
+// for g=128, 8 for g=64) of one weight row with a buffer load whose group
+// offset is scalar; the four lane groups of 16 cover one whole group of that
+// row. D groups are in flight per wave; they stay in flight across the
+// workgroup barriers (the barrier waits only for LDS traffic).
 //
 // Dequantisation builds exact fp16 integers in registers: for a 32-bit word
 // holding nibbles n0..n7, (w & 0x000F000F) | 0x64006400 is the fp16 pair
 // (1024 + n0, 1024 + n4) and (w & 0x00F000F0) | 0x54005400 is (64 + n1,
 // 64 + n5); the same on w >> 8 gives n2/n6 and n3/n7. One packed fp16
 // subtract of (1024 + z) or (64 + z) leaves the exact integers q - z. The
-// MFMA B operand therefore holds K positions in the order
-// [0,4,1,5,2,6,3,7] within each 8; a contraction is unchanged by the same
-// permutation on both operands, so the activation rows are stored in LDS
-// with that same order and no weight preshuffle is needed.
+// MFMA B operand therefore holds K positions in the order [0,4,1,5,2,6,3,7]
+// within each 8. A contraction is unchanged by the same permutation on both
+// operands, so the activations are consumed in that same order: x is
+// permuted once per forward by the preparation kernel and H is written
+// permuted by gate_up's epilogue. No weight preshuffle is needed.
 //
 // v_mfma_f32_16x16x32_f16 accumulates one group (g/32 MFMAs) into a fresh
 // fp32 partial; the group's scale is applied once per output in fp32
 // (acc += s * partial). The scale never touches an fp16 weight, so the only
 // rounding is the fp32 accumulation.
 //
-// Activations: the tile's 32 rows are staged through LDS in K chunks of
-// D groups (gathered rows of x for gate_up, rows of H for down), loaded into
-// registers one chunk ahead. Scale and zero point of each (row, group) are
-// loaded with the weight fragment, D groups ahead.
+// Activations: the tile's 32 rows are staged through LDS, either in K chunks
+// of 512 (double-buffered, loaded into registers one chunk ahead; gate_up)
+// or the whole K at once (down, K = m). Scale and zero point of the
+// workgroup's rows are copied into LDS once, as contiguous row ranges.
 //
 // Epilogues: gate_up computes gelu_tanh(gate) * up in fp32 and writes H in
-// fp16 at the tile's padded row; down writes fp32 Y at the assignment's flat
-// slot t * topk + k, which the combine reads in ascending k.
+// fp16 at the tile's padded row (permuted per 8 columns, see above); down
+// writes fp32 Y at the assignment's flat slot t * topk + k, which the combine
+// reads in ascending k.
 #include "dgw4_internal.hpp"
+
+#include <type_traits>
 
 namespace dgw4 {
 namespace {
@@ -54,22 +59,26 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTilesPerWave = 2;                        // MFMA column tiles per wave
-constexpr int kRowsPerWG = kWaves * kTilesPerWave * 16; // weight rows per workgroup
-constexpr int kStages = 4;                              // groups in flight per wave
+constexpr int kTilesPerWave = 2;         // MFMA column tiles (16 weight rows each) per wave
+constexpr int kChunkK = 512;             // activation K per LDS chunk (chunked staging)
+constexpr int kChunkSeg = kChunkK / 8;   // 16-byte segments per row and chunk
+constexpr int kChunkPitch = kChunkSeg + 1;   // +16 B per row: spreads LDS banks
+constexpr int kSingleK = 1024;           // largest K staged at once (one loop-free pass)
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // a voffset no buffer here reaches
 
-// Activation chunk geometry for group size G: one chunk = kStages groups.
-template <int G>
-struct Chunk {
-    static constexpr int K = kStages * G;                 // activation K per LDS chunk
-    static constexpr int Seg = K / 8;                     // 16-byte segments per row
-    static constexpr int Pitch = Seg + 1;                 // +16 B per row: spreads banks
-    static constexpr int Lds = kBlockM * Pitch;           // uint4 entries
-    static constexpr int Loads = kBlockM * Seg / kThreads;  // 16-byte loads per thread
-};
+// Raw buffer resource over [base, base + bytes): reads past the end return 0.
+__device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ inline uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
 template <int G>
 struct Frag;                     // one lane's share of one group of one weight row
@@ -79,13 +88,13 @@ template <>
 struct Frag<64> { uint2 v; };    // 8 bytes = 16 nibbles
 
 template <int G>
-__device__ inline Frag<G> load_frag(const uint8_t *p)
+__device__ inline Frag<G> load_frag(rsrc_t r, uint32_t voff, uint32_t soff)
 {
     Frag<G> f;
     if constexpr (G == 128)
-        f.v = *reinterpret_cast<const uint4 *>(p);
+        f.v = load16(r, voff, soff);
     else
-        f.v = *reinterpret_cast<const uint2 *>(p);
+        f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
     return f;
 }
 
@@ -100,29 +109,27 @@ __device__ inline uint32_t frag_word(const Frag<G> &f, int t)
 
 __device__ inline f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
+// (w & mask) | magic in one v_and_or_b32 (gfx9 VOP3 takes no literal, so the
+// compiler would otherwise split it). The result only feeds ordinary VALU.
+__device__ inline uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(magic));
+    return r;
+}
+
 // 8 nibbles -> 8 exact fp16 values (q - z) in K order [0,4,1,5,2,6,3,7].
 __device__ inline f16x8 dequant8(uint32_t w, f16x2 c1024, f16x2 c64)
 {
     const uint32_t w8 = w >> 8;
-    const f16x2 a = as_h2((w & 0x000F000Fu) | 0x64006400u) - c1024;
-    const f16x2 b = as_h2((w & 0x00F000F0u) | 0x54005400u) - c64;
-    const f16x2 c = as_h2((w8 & 0x000F000Fu) | 0x64006400u) - c1024;
-    const f16x2 d = as_h2((w8 & 0x00F000F0u) | 0x54005400u) - c64;
+    const f16x2 a = as_h2(and_or(w, 0x000F000Fu, 0x64006400u)) - c1024;
+    const f16x2 b = as_h2(and_or(w, 0x00F000F0u, 0x54005400u)) - c64;
+    const f16x2 c = as_h2(and_or(w8, 0x000F000Fu, 0x64006400u)) - c1024;
+    const f16x2 d = as_h2(and_or(w8, 0x00F000F0u, 0x54005400u)) - c64;
     f16x8 r;
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
     r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
     return r;
-}
-
-// 8 consecutive fp16 values -> the same values in order [0,4,1,5,2,6,3,7].
-__device__ inline uint4 permute8(uint4 v)
-{
-    uint4 o;
-    o.x = (v.x & 0xFFFFu) | (v.z << 16);
-    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
-    o.z = (v.y & 0xFFFFu) | (v.w << 16);
-    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
-    return o;
 }
 
 __device__ inline float gelu_tanh(float v)
@@ -132,173 +139,174 @@ __device__ inline float gelu_tanh(float v)
     return 0.5f * v * (1.0f + tanhf(k0 * (v + k1 * v * v * v)));
 }
 
-// Weight row (within the expert) of column tile tt of wave w in N-block nb.
-template <bool GATED>
-__device__ inline int weight_row(int nb, int w, int tt, int n_out)
+// Position of column c inside its row when a row is stored permuted per 8
+// (the inverse of the K order [0,4,1,5,2,6,3,7]).
+__device__ inline int permuted_col(int c)
 {
-    if constexpr (GATED)    // tile 0: gate rows, tile 1: the matching up rows
-        return nb * (kWaves * 16) + w * 16 + tt * n_out;
-    else
-        return nb * (kWaves * kTilesPerWave * 16) + w * (kTilesPerWave * 16) + tt * 16;
+    const int j = c & 7;
+    return (c & ~7) | ((j & 3) << 1) | (j >> 2);
 }
 
-template <int G, bool GATED>
-__global__ void __launch_bounds__(kThreads) moe_gemm_kernel(GemmArgs p)
+// At least two waves per SIMD: the register budget is 256 VGPRs per wave.
+template <int G, bool GATED, int WAVES, bool SINGLE>
+__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
+moe_gemm_kernel(GemmArgs p)
 {
-    constexpr int D = kStages;
-    constexpr int kChunkK = Chunk<G>::K;
-    constexpr int kSegPerRow = Chunk<G>::Seg;
-    constexpr int kPitch = Chunk<G>::Pitch;
-    constexpr int kStageLoads = Chunk<G>::Loads;
-    constexpr int kWords = G / 32;          // MFMA K steps per group = words per fragment
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kWords = G / 32;                 // MFMA K steps per group = words per fragment
+    constexpr int CG = kChunkK / G;                // groups per activation chunk
+    // weight groups in flight per wave: all of K when staged at once, else two chunks
+    constexpr int D = SINGLE ? kSingleK / G : 2 * CG;
+    constexpr int kRangeRows = WAVES * 16;         // rows of each scale/zero range
+    constexpr int kChunkLoads = kBlockM * kChunkSeg / kThreads;
     const int nb = blockIdx.x;
     const int tile = blockIdx.y;
     const int total = *p.num_padded;
     if (tile * kBlockM >= total)
         return;
     const int e = p.tile_expert[tile];
-    const int row0 = tile * kBlockM;        // first padded row of this tile
+    const int row0 = tile * kBlockM;               // first padded row of this tile
     const int valid = min(kBlockM, p.counts[e] - (row0 - p.offsets[e]));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int K = p.K;
-    const int NG = K / G;
-    const int NC = (K + kChunkK - 1) / kChunkK;
-
-    __shared__ uint4 lds_a[Chunk<G>::Lds];  // [kBlockM][kPitch], K order permuted per 8
-
-    // columns owned by this wave; a wave past the edge only helps with staging
-    const int col_first = GATED ? nb * (kWaves * 16) + wave * 16
-                                : nb * (kWaves * kTilesPerWave * 16) + wave * (kTilesPerWave * 16);
-    const bool wave_live = col_first < p.n_out;
-
-    // ---- activation rows of the tile: source row per tile row, -1 past `valid`
-    // gate_up: x row of token sorted_id / topk; down: H row at the padded position
-    __shared__ int s_src[kBlockM];
-    if (tid < kBlockM) {
-        int src = -1;
-        if (tid < valid) {
-            if constexpr (GATED)
-                src = p.sorted_ids[row0 + tid] / p.topk;
-            else
-                src = row0 + tid;
-        }
-        s_src[tid] = src;
-    }
-    __syncthreads();
-    // all loads below are unconditional with addresses clamped into the source;
-    // rows past `valid` and K past the end become zeros when stored to LDS
-    const uint16_t *arow[kStageLoads];
-    int aseg[kStageLoads];
-    bool arow_ok[kStageLoads];
-#pragma unroll
-    for (int i = 0; i < kStageLoads; ++i) {
-        const int lin = i * kThreads + tid;
-        const int src = s_src[lin / kSegPerRow];
-        aseg[i] = lin % kSegPerRow;
-        arow_ok[i] = src >= 0;
-        arow[i] = p.a_src + (size_t)(src >= 0 ? src : 0) * K;
-    }
-    uint4 xr[kStageLoads];
-    auto load_chunk = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < kStageLoads; ++i) {
-            const int k = min(c * kChunkK + aseg[i] * 8, K - 8);
-            xr[i] = *reinterpret_cast<const uint4 *>(arow[i] + k);
-        }
-    };
-    auto store_chunk = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < kStageLoads; ++i) {
-            const int lin = i * kThreads + tid;
-            // zero by mask, not by a branch, so the load is never sunk into one
-            const uint32_t keep =
-                (arow_ok[i] && (c * kChunkK + aseg[i] * 8 < K)) ? 0xFFFFFFFFu : 0u;
-            uint4 v = permute8(xr[i]);
-            v.x &= keep;
-            v.y &= keep;
-            v.z &= keep;
-            v.w &= keep;
-            lds_a[(lin / kSegPerRow) * kPitch + aseg[i]] = v;
-        }
-    };
-
-    // ---- weight fragments: lane -> (row within the column tile, quarter of the group)
     const int lrow = lane & 15;
     const int quarter = lane >> 4;
-    const size_t expert_row0 = (size_t)e * p.n_w;
-    const uint8_t *wptr[kTilesPerWave];
-    const uint16_t *sptr[kTilesPerWave];
-    const uint16_t *zptr[kTilesPerWave];
+    const int K = p.K;
+    const int NG = K / G;
+    const size_t wexp = (size_t)e * p.n_w;
+
+    // columns owned by this wave; a wave past the edge runs the same loads and
+    // math on row 0 of the expert and stores nothing
+    const int col_first = GATED ? nb * (WAVES * 16) + wave * 16
+                                : nb * (WAVES * 32) + wave * 32;
+    const bool wave_live = col_first < p.n_out;
+    // the two scale/zero row ranges of this workgroup (each kRangeRows rows)
+    const int range0 = GATED ? nb * (WAVES * 16) : nb * (WAVES * 32);
+    const int range1 = GATED ? p.n_out + range0 : range0 + kRangeRows;
+
+    extern __shared__ uint4 lds[];
+    // [A buffers][scale][zero]: A is [kBlockM][pitch] uint4, scale/zero are
+    // [2 * kRangeRows][NG] fp16
+    const int a_pitch = SINGLE ? K / 8 + 1 : kChunkPitch;
+    const int a_entries = SINGLE ? kBlockM * a_pitch : 2 * kBlockM * kChunkPitch;
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + a_entries);
+    uint16_t *lds_z = lds_s + 2 * kRangeRows * NG;
+    __shared__ int s_src[kBlockM];
+
+    // ---- 1. loads that need nothing but the tile: scale/zero ranges and the
+    // tile's row ids. Issued before the weight prefetch so waiting on them
+    // does not wait on weights.
+    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    const int range_dw = kRangeRows * NG / 2;      // dwords per range (NG * rows is even)
+    constexpr int kSzPerThread = 8;
+    uint32_t sv[kSzPerThread], zv[kSzPerThread];
+    const int sz_total = 2 * range_dw;
+    auto sz_off = [&](int x) -> uint32_t {
+        if (x >= sz_total)
+            return kOutOfRange;
+        const int r = x >= range_dw;
+        return (uint32_t)((r ? range1 : range0) * NG) * 2u + (uint32_t)(x - r * range_dw) * 4u;
+    };
+#pragma unroll
+    for (int i = 0; i < kSzPerThread; ++i) {
+        const uint32_t off = sz_off(i * kThreads + tid);
+        sv[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+    }
+    int fid = 0;
+    if (GATED && tid < kBlockM)
+        fid = p.sorted_ids[row0 + tid];            // row0 + tid < cap: always in the buffer
+
+    // ---- 2. weight prefetch, D groups
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
+    uint32_t wvoff[kTilesPerWave];
+    int lds_row[kTilesPerWave];                    // this lane's row in the scale/zero ranges
 #pragma unroll
     for (int tt = 0; tt < kTilesPerWave; ++tt) {
-        int wr = weight_row<GATED>(nb, wave, tt, p.n_out) + lrow;
-        if (!wave_live)
-            wr = 0;                           // keeps idle waves' pointers in bounds
-        wptr[tt] = p.q + (expert_row0 + wr) * (size_t)(K / 2) + quarter * (G / 8);
-        sptr[tt] = p.s + (expert_row0 + wr) * (size_t)NG;
-        zptr[tt] = p.z + (expert_row0 + wr) * (size_t)NG;
+        const int in_range = GATED ? wave * 16 + lrow : wave * 32 + tt * 16 + lrow;
+        const int wr = (GATED ? (tt ? range1 : range0) : range0) + in_range;
+        wvoff[tt] = wave_live ? (uint32_t)wr * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8))
+                              : (uint32_t)(quarter * (G / 8));
+        lds_row[tt] = GATED ? tt * kRangeRows + in_range : in_range;
     }
     Frag<G> bq[D][kTilesPerWave];
-    uint32_t bs[D][kTilesPerWave], bz[D][kTilesPerWave];
     auto prefetch = [&](int s, int gi) {      // group gi (clamped) into stage s
         gi = min(gi, NG - 1);
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt) {
-            bq[s][tt] = load_frag<G>(wptr[tt] + gi * (G / 2));
-            bs[s][tt] = sptr[tt][gi];
-            bz[s][tt] = zptr[tt][gi];
-        }
+        for (int tt = 0; tt < kTilesPerWave; ++tt)
+            bq[s][tt] = load_frag<G>(rq, wvoff[tt], (uint32_t)(gi * (G / 2)));
     };
-
-    // activation chunk 0 first, so storing it to LDS waits for these loads only.
-    // Idle waves (past the N edge) run the same loads and math on row 0 of the
-    // expert and store nothing: no branch separates the loads from their uses.
-    load_chunk(0);
-    __builtin_amdgcn_sched_barrier(0);        // keep the activation loads first in issue order
 #pragma unroll
     for (int s = 0; s < D; ++s)
         prefetch(s, s);
-    store_chunk(0);                           // read only after the loop's first barrier
+    __builtin_amdgcn_sched_barrier(0);
 
+    // ---- 3. scale/zero and row sources into LDS
+    {
+        uint32_t *ls = reinterpret_cast<uint32_t *>(lds_s);
+        uint32_t *lz = reinterpret_cast<uint32_t *>(lds_z);
+#pragma unroll
+        for (int i = 0; i < kSzPerThread; ++i) {
+            const int x = i * kThreads + tid;
+            if (x < sz_total) {
+                ls[x] = sv[i];
+                lz[x] = zv[i];
+            }
+        }
+        for (int x = kSzPerThread * kThreads + tid; x < sz_total; x += kThreads) {
+            ls[x] = __builtin_amdgcn_raw_buffer_load_b32(rs, sz_off(x), 0, 0);   // large NG only
+            lz[x] = __builtin_amdgcn_raw_buffer_load_b32(rz, sz_off(x), 0, 0);
+        }
+    }
+    if (tid < kBlockM)
+        s_src[tid] = tid < valid ? (GATED ? fid / p.topk : row0 + tid) : -1;
+    __syncthreads();
+
+    // ---- 4. activation staging (sources are already in the permuted K order)
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
+    uint4 *lds_a = lds;
     f32x4 acc[kTilesPerWave][2];
 #pragma unroll
     for (int tt = 0; tt < kTilesPerWave; ++tt)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
             acc[tt][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const bool two_blocks = valid > 16;       // second 16-row MFMA block has rows
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+    const f16x2 k64 = {(_Float16)64.0f, (_Float16)64.0f};
 
-    // one group from stage s: dequantise, 2 x g/32 MFMAs per row block, scale fold
-    auto group = [&](int s) {
+    // group gi from stage s over NMS 16-row blocks, reading activations at
+    // 16-byte segment seg0 (+ lane offsets) of the LDS rows starting at abuf
+    // A group past the last one (gi >= NG, in a padded trip) contributes
+    // exactly nothing: its scale is taken as 0 and every index is clamped.
+    auto group = [&](int s, const uint4 *abuf, int pitch, int seg0, int gi, auto nms_tag) {
+        constexpr int NMS = decltype(nms_tag)::value;
         f16x2 c1024[kTilesPerWave], c64[kTilesPerWave];
         float scale[kTilesPerWave];
+        const int gc = min(gi, NG - 1);
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt) {
-            scale[tt] = (float)__builtin_bit_cast(_Float16, (uint16_t)bs[s][tt]);
-            const float zf = (float)__builtin_bit_cast(_Float16, (uint16_t)bz[s][tt]);
-            const _Float16 a = (_Float16)(1024.0f + zf);
-            const _Float16 b = (_Float16)(64.0f + zf);
-            c1024[tt] = f16x2{a, a};
-            c64[tt] = f16x2{b, b};
+            const uint32_t zb = lds_z[lds_row[tt] * NG + gc];
+            const f16x2 zz = as_h2(zb | (zb << 16));
+            c1024[tt] = zz + k1024;          // fp16(1024 + z), exact for |z| <= 1024
+            c64[tt] = zz + k64;
+            const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
+            scale[tt] = gi < NG ? sc : 0.0f;
         }
-        f32x4 part[kTilesPerWave][2];
+        f32x4 part[kTilesPerWave][NMS];
 #pragma unroll
         for (int t = 0; t < kWords; ++t) {
             f16x8 bop[kTilesPerWave];
 #pragma unroll
             for (int tt = 0; tt < kTilesPerWave; ++tt)
                 bop[tt] = dequant8(frag_word<G>(bq[s][tt], t), c1024[tt], c64[tt]);
-            // this lane's 8 K positions inside the chunk
-            const int seg = s * (G / 8) + quarter * (G / 32) + t;
+            const int seg = seg0 + quarter * (G / 32) + t;   // this lane's 8 K positions
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-                if (ms == 1 && !two_blocks)
-                    continue;
-                const f16x8 aop = __builtin_bit_cast(f16x8, lds_a[(ms * 16 + lrow) * kPitch + seg]);
+            for (int ms = 0; ms < NMS; ++ms) {
+                const f16x8 aop = __builtin_bit_cast(f16x8, abuf[(ms * 16 + lrow) * pitch + seg]);
 #pragma unroll
                 for (int tt = 0; tt < kTilesPerWave; ++tt)
                     part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -308,34 +316,108 @@ __global__ void __launch_bounds__(kThreads) moe_gemm_kernel(GemmArgs p)
 #pragma unroll
         for (int tt = 0; tt < kTilesPerWave; ++tt)
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
-                if (ms == 1 && !two_blocks)
-                    continue;
+            for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     acc[tt][ms][i] += scale[tt] * part[tt][ms][i];
-            }
     };
 
-    // all chunks but the last: every group exists, prefetch D groups ahead
-    for (int c = 0; c + 1 < NC; ++c) {
-        load_chunk(c + 1);                    // registers; written to LDS after compute
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();                      // chunk c is in LDS
+    if constexpr (SINGLE) {
+        // the whole K of the tile's rows, once; every weight group of the wave
+        // is already in flight (D >= NG), so there is no loop at all
+        const int seg_row = K / 8;
+        const int n = kBlockM * seg_row;
+        for (int x0 = 0; x0 < n; x0 += 8 * kThreads) {
+            uint4 v[8];
 #pragma unroll
-        for (int s = 0; s < D; ++s) {
-            group(s);
-            prefetch(s, (c + 1) * D + s);
+            for (int i = 0; i < 8; ++i) {
+                const int x = x0 + i * kThreads + tid;
+                const int r = min(x / seg_row, kBlockM - 1), sg = x - r * seg_row;
+                const int src = x < n ? s_src[r] : -1;
+                v[i] = load16(ra, src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + (uint32_t)sg * 16u
+                                           : kOutOfRange, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int x = x0 + i * kThreads + tid;
+                const int r = min(x / seg_row, kBlockM - 1), sg = x - r * seg_row;
+                if (x < n)
+                    lds_a[r * a_pitch + sg] = v[i];
+            }
         }
-        __syncthreads();                      // everyone is done reading chunk c
-        store_chunk(c + 1);
-    }
-    // last chunk: groups may stop early, nothing left to prefetch
-    __syncthreads();
+        __syncthreads();
+        auto run = [&](auto nms_tag) {
+            // all loads were issued before this point, so skipping the groups
+            // past NG cannot change the wait counts
 #pragma unroll
-    for (int s = 0; s < D; ++s)
-        if ((NC - 1) * D + s < NG)
-            group(s);
+            for (int gi = 0; gi < D; ++gi)
+                if (gi < NG)
+                    group(gi, lds_a, a_pitch, gi * (G / 8), gi, nms_tag);
+        };
+        if (valid > 16)
+            run(std::integral_constant<int, 2>{});
+        else
+            run(std::integral_constant<int, 1>{});
+    } else {
+        const int NC = (K + kChunkK - 1) / kChunkK;
+        static_assert(kThreads % kChunkSeg == 0, "a thread keeps one 16-byte column of a chunk");
+        constexpr int kRowStep = kThreads / kChunkSeg;
+        const int aseg = tid % kChunkSeg;         // this thread's 16-byte column of a chunk
+        const int arow0 = tid / kChunkSeg;        // and its rows arow0 + i * kRowStep
+        uint4 xr[kChunkLoads];
+        auto load_chunk = [&](int c) {            // rows past `valid` and K past the end read 0
+            const bool in_k = c * kChunkK + aseg * 8 < K;
+            const uint32_t col = (uint32_t)(c * kChunkK + aseg * 8) * 2u;
+#pragma unroll
+            for (int i = 0; i < kChunkLoads; ++i) {
+                const int src = s_src[arow0 + i * kRowStep];
+                xr[i] = load16(ra, in_k && src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + col
+                                                    : kOutOfRange, 0);
+            }
+        };
+        auto store_chunk = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < kChunkLoads; ++i)
+                lds_a[buf * kBlockM * kChunkPitch + (arow0 + i * kRowStep) * kChunkPitch + aseg] =
+                    xr[i];
+        };
+        load_chunk(0);
+        store_chunk(0);                           // read only after the loop's first barrier
+        // Two chunks per trip so that every register stage index is static. Per
+        // chunk: load the next activation chunk into registers, one barrier (this
+        // chunk is in LDS, the other buffer is free), the chunk's groups with
+        // their prefetch two chunks ahead, then store the next chunk.
+        // Two chunks per trip so that every register stage index is static, and
+        // no branch inside a trip (an odd chunk count runs one padded chunk
+        // whose activations read as zero and whose groups have scale 0), so
+        // the wait counts the compiler derives stay exact. Per chunk: load the
+        // next activation chunk into registers, one barrier (this chunk is in
+        // LDS, the other buffer is free), the chunk's groups each followed by
+        // the prefetch of the group two chunks ahead, then store the next chunk.
+        auto run = [&](auto nms_tag) {
+            for (int c0 = 0; c0 < NC; c0 += 2) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int c = c0 + half;
+                    load_chunk(c + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    __syncthreads();
+                    const uint4 *abuf = lds_a + half * kBlockM * kChunkPitch;
+#pragma unroll
+                    for (int cs = 0; cs < CG; ++cs) {
+                        const int gi = c * CG + cs;
+                        group(half * CG + cs, abuf, kChunkPitch, cs * (G / 8), gi, nms_tag);
+                        prefetch(half * CG + cs, gi + D);
+                    }
+                    store_chunk(half ^ 1);
+                }
+            }
+        };
+        if (valid > 16)
+            run(std::integral_constant<int, 2>{});
+        else
+            run(std::integral_constant<int, 1>{});
+    }
 
     if (!wave_live)
         return;
@@ -351,40 +433,81 @@ __global__ void __launch_bounds__(kThreads) moe_gemm_kernel(GemmArgs p)
                 const int col = col_first + lrow;
                 const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
                 uint16_t *H = static_cast<uint16_t *>(p.out);
-                H[(size_t)(row0 + r) * p.n_out + col] =
+                H[(size_t)(row0 + r) * p.n_out + permuted_col(col)] =
                     __builtin_bit_cast(uint16_t, (_Float16)h);
             } else {
-                const int fid = p.sorted_ids[row0 + r];
+                const int f = p.sorted_ids[row0 + r];
                 float *Y = static_cast<float *>(p.out);
 #pragma unroll
                 for (int tt = 0; tt < kTilesPerWave; ++tt)
-                    Y[(size_t)fid * p.n_out + col_first + tt * 16 + lrow] = acc[tt][ms][i];
+                    Y[(size_t)f * p.n_out + col_first + tt * 16 + lrow] = acc[tt][ms][i];
             }
         }
     }
 }
 
-template <int G, bool GATED>
+// Shape of each launch: gate_up streams K = d in chunks with 4 waves per
+// workgroup; down stages its whole K = m once (when m <= kSingleK) and shares
+// it among 8 waves.
+template <bool GATED, bool SINGLE>
+struct Shape {
+    static constexpr int kWaves = GATED ? 4 : 8;
+};
+
+template <int G, bool GATED, bool SINGLE>
+size_t lds_bytes(int K)
+{
+    constexpr int W = Shape<GATED, SINGLE>::kWaves;
+    const size_t a = SINGLE ? (size_t)kBlockM * (K / 8 + 1) : (size_t)2 * kBlockM * kChunkPitch;
+    return sizeof(uint4) * a + 2 * sizeof(uint16_t) * 2 * (W * 16) * (size_t)(K / G);
+}
+
+template <int G, bool GATED, bool SINGLE>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 {
-    const int cols_per_wg = GATED ? kWaves * 16 : kWaves * kTilesPerWave * 16;
+    constexpr int W = Shape<GATED, SINGLE>::kWaves;
+    const int cols_per_wg = GATED ? W * 16 : W * 32;
     const int nblocks = (a.n_out + cols_per_wg - 1) / cols_per_wg;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    moe_gemm_kernel<G, GATED><<<dim3(nblocks, a.max_tiles), dim3(kThreads), 0, stream>>>(a);
+    const size_t lds = lds_bytes<G, GATED, SINGLE>(a.K);
+    auto kern = moe_gemm_kernel<G, GATED, W, SINGLE>;
+    static size_t lds_allowed = 64 * 1024;   // raised once per instantiation when needed
+    if (lds > lds_allowed) {
+        hipError_t err = hipFuncSetAttribute((const void *)kern,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess)
+            return err;
+        lds_allowed = lds;
+    }
+    kern<<<dim3(nblocks, a.max_tiles), dim3(W * 64), lds, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
+size_t gemm_lds_bytes(bool gated, int K, int g)
+{
+    if (gated)
+        return g == 128 ? lds_bytes<128, true, false>(K) : lds_bytes<64, true, false>(K);
+    if (K <= kSingleK)
+        return g == 128 ? lds_bytes<128, false, true>(K) : lds_bytes<64, false, true>(K);
+    return g == 128 ? lds_bytes<128, false, false>(K) : lds_bytes<64, false, false>(K);
+}
+
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
-    return g == 128 ? launch_gemm<128, true>(a, stream) : launch_gemm<64, true>(a, stream);
+    return g == 128 ? launch_gemm<128, true, false>(a, stream)
+                    : launch_gemm<64, true, false>(a, stream);
 }
 
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
 {
-    return g == 128 ? launch_gemm<128, false>(a, stream) : launch_gemm<64, false>(a, stream);
+    if (a.K <= kSingleK)
+        return g == 128 ? launch_gemm<128, false, true>(a, stream)
+                        : launch_gemm<64, false, true>(a, stream);
+    return g == 128 ? launch_gemm<128, false, false>(a, stream)
+                    : launch_gemm<64, false, false>(a, stream);
 }
 
 }  // namespace dgw4
