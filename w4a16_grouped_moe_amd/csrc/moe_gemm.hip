@@ -65,7 +65,7 @@ constexpr int kTilesPerWave = 2;         // MFMA column tiles (16 weight rows ea
 constexpr int kChunkK = 512;             // activation K per LDS chunk (chunked staging)
 constexpr int kChunkSeg = kChunkK / 8;   // 16-byte segments per row and chunk
 constexpr int kChunkPitch = kChunkSeg + 1;   // +16 B per row: spreads LDS banks
-constexpr int kSingleK = 1024;           // largest K staged at once (one loop-free pass)
+constexpr int kSingleK = 768;            // largest K staged at once (one loop-free pass)
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // a voffset no buffer here reaches
 
 // Raw buffer resource over [base, base + bytes): reads past the end return 0.
@@ -147,10 +147,11 @@ __device__ inline int permuted_col(int c)
     return (c & ~7) | ((j & 3) << 1) | (j >> 2);
 }
 
-// At least two waves per SIMD: the register budget is 256 VGPRs per wave.
+// Register budget: 8-wave workgroups (down) get 4 waves per SIMD (128 VGPRs)
+// so that two workgroups share a CU; 4-wave ones get 2 (256 VGPRs).
 template <int G, bool GATED, int WAVES, bool SINGLE>
-__global__ void __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
-moe_gemm_kernel(GemmArgs p)
+__global__ void __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArgs p)
 {
     constexpr int kThreads = WAVES * 64;
     constexpr int kWords = G / 32;                 // MFMA K steps per group = words per fragment
@@ -170,7 +171,7 @@ moe_gemm_kernel(GemmArgs p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int lrow = lane & 15;
     const int quarter = lane >> 4;
     const int K = p.K;
@@ -383,10 +384,6 @@ moe_gemm_kernel(GemmArgs p)
         };
         load_chunk(0);
         store_chunk(0);                           // read only after the loop's first barrier
-        // Two chunks per trip so that every register stage index is static. Per
-        // chunk: load the next activation chunk into registers, one barrier (this
-        // chunk is in LDS, the other buffer is free), the chunk's groups with
-        // their prefetch two chunks ahead, then store the next chunk.
         // Two chunks per trip so that every register stage index is static, and
         // no branch inside a trip (an odd chunk count runs one padded chunk
         // whose activations read as zero and whose groups have scale 0), so
