@@ -152,6 +152,7 @@ DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int blo
  *   d, m       d % gu_g == 0, m % dn_g == 0 (so both are multiples of 64)
  *   gu_q/s/z   device, gate_up stack [E, 2m, d] packed with group gu_g
  *   dn_q/s/z   device, down stack [E, d, m] packed with group dn_g
+ *              (x, the six pack pointers: 16-byte aligned; out: 8-byte aligned)
  *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED)
  *   workspace  device scratch of at least *ws_bytes bytes, 256-byte aligned.
  *              If workspace is NULL, the required size is written to

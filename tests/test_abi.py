@@ -64,6 +64,8 @@ def _fwd(**kw):
     (dict(dg=96), B.ERR_UNSUPPORTED),
     (dict(ws=(1 << 12) + 4), B.ERR_INVALID_ARG),  # misaligned workspace
     (dict(x=(1 << 12) + 2), B.ERR_INVALID_ARG),   # misaligned x
+    (dict(gs=(1 << 12) + 8), B.ERR_INVALID_ARG),  # scale/zero arrays are read 16 bytes at a time
+    (dict(dz=(1 << 12) + 2), B.ERR_INVALID_ARG),
     (dict(n=16), B.ERR_WORKSPACE),
     (dict(T=-1), B.ERR_INVALID_ARG),
 ])

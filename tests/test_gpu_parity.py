@@ -120,6 +120,9 @@ def test_forward_tiny_every_element():
     dict(name="top1", E=1, topk=1, T=45, d=256, m=256, g_dn=128),
     # one token
     dict(name="one_token", E=16, topk=4, T=1, d=512, m=192),
+    # m > 768: down streams K = m in chunks (odd chunk count, odd group count);
+    # gate_up's last N-block has idle waves (1088 = 8.5 x 128)
+    dict(name="long_m", E=4, topk=2, T=50, d=384, m=1088),
 ])
 def test_forward_shapes_every_element(case):
     shp = lc.custom_shape(**case)

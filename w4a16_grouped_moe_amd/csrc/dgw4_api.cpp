@@ -166,7 +166,8 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     if (T > 0 && (!x || !topk_ids || !topk_w || !out))
         return DGW4_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign) || !aligned(x, 16) || !aligned(gu_q, 16) ||
-        !aligned(dn_q, 16) || !aligned(out, 8))
+        !aligned(dn_q, 16) || !aligned(gu_s, 16) || !aligned(gu_z, 16) || !aligned(dn_s, 16) ||
+        !aligned(dn_z, 16) || !aligned(out, 8))
         return DGW4_ERR_INVALID_ARG;
     if (*ws_bytes < L.total)
         return DGW4_ERR_WORKSPACE;

@@ -61,10 +61,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kTilesPerWave = 2;         // MFMA column tiles (16 weight rows each) per wave
-constexpr int kChunkK = 512;             // activation K per LDS chunk (chunked staging)
-constexpr int kChunkSeg = kChunkK / 8;   // 16-byte segments per row and chunk
-constexpr int kChunkPitch = kChunkSeg + 1;   // +16 B per row: spreads LDS banks
 constexpr int kSingleK = 768;            // largest K staged at once (one loop-free pass)
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // a voffset no buffer here reaches
 
@@ -147,19 +143,47 @@ __device__ inline int permuted_col(int c)
     return (c & ~7) | ((j & 3) << 1) | (j >> 2);
 }
 
-// Register budget: 8-wave workgroups (down) get 4 waves per SIMD (128 VGPRs)
-// so that two workgroups share a CU; 4-wave ones get 2 (256 VGPRs).
-template <int G, bool GATED, int WAVES, bool SINGLE>
-__global__ void __launch_bounds__(WAVES * 64)
-__attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArgs p)
+// Launch shape of one GEMM kernel instantiation.
+//   kWaves    waves per workgroup
+//   kTiles    MFMA column tiles (16 weight rows each) per wave; gated: gate and
+//             up tiles alternate (tile 2p = gate rows, 2p + 1 = the matching
+//             up rows), so a wave owns kTiles / 2 * 16 output columns
+//   kChunkK   activation K per LDS chunk (0: the whole K staged at once)
+//   kAhead    activation chunks of weight groups kept in flight per wave
+//   kWpe      waves per SIMD the register budget is sized for
+template <int W, int T, int CK, int AH, int WPE>
+struct Shape {
+    static constexpr int kWaves = W;
+    static constexpr int kTiles = T;
+    static constexpr int kChunkK = CK;
+    static constexpr int kAhead = AH;
+    static constexpr int kWpe = WPE;
+};
+
+template <int G, bool GATED, class S>
+__global__ void __launch_bounds__(S::kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
 {
+    constexpr int WAVES = S::kWaves;
+    constexpr int TPW = S::kTiles;
+    constexpr bool SINGLE = S::kChunkK == 0;
     constexpr int kThreads = WAVES * 64;
     constexpr int kWords = G / 32;                 // MFMA K steps per group = words per fragment
+    constexpr int kChunkK = SINGLE ? G : S::kChunkK;
+    constexpr int kChunkSeg = kChunkK / 8;         // 16-byte segments per row and chunk
+    constexpr int kChunkPitch = kChunkSeg + 1;     // +16 B per row: spreads LDS banks
     constexpr int CG = kChunkK / G;                // groups per activation chunk
-    // weight groups in flight per wave: all of K when staged at once, else two chunks
-    constexpr int D = SINGLE ? kSingleK / G : 2 * CG;
-    constexpr int kRangeRows = WAVES * 16;         // rows of each scale/zero range
+    // weight groups in flight per wave: all of K when staged at once, else
+    // kAhead chunks
+    constexpr int D = SINGLE ? kSingleK / G : S::kAhead * CG;
+    // chunks per loop trip: register stages and the two LDS buffers both
+    // repeat with it, so every index is static inside a trip
+    constexpr int TRIP = S::kAhead % 2 == 0 ? S::kAhead : 2 * S::kAhead;
+    constexpr int kColsPerWave = GATED ? TPW / 2 * 16 : TPW * 16;
+    constexpr int kColsPerWg = WAVES * kColsPerWave;
+    constexpr int kRangeRows = WAVES * TPW * 8;    // rows of each scale/zero range
     constexpr int kChunkLoads = kBlockM * kChunkSeg / kThreads;
+    static_assert(!GATED || TPW % 2 == 0, "gated tiles come in gate/up pairs");
     const int nb = blockIdx.x;
     const int tile = blockIdx.y;
     const int total = *p.num_padded;
@@ -178,13 +202,14 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
     const int NG = K / G;
     const size_t wexp = (size_t)e * p.n_w;
 
-    // columns owned by this wave; a wave past the edge runs the same loads and
-    // math on row 0 of the expert and stores nothing
-    const int col_first = GATED ? nb * (WAVES * 16) + wave * 16
-                                : nb * (WAVES * 32) + wave * 32;
+    // columns owned by this wave. A wave past the edge (n_out is a multiple
+    // of its width) runs the same code on an empty weight buffer: its loads
+    // return zeros without touching memory, and it stores nothing.
+    const int col_first = nb * kColsPerWg + wave * kColsPerWave;
     const bool wave_live = col_first < p.n_out;
-    // the two scale/zero row ranges of this workgroup (each kRangeRows rows)
-    const int range0 = GATED ? nb * (WAVES * 16) : nb * (WAVES * 32);
+    // the two scale/zero row ranges of this workgroup (each kRangeRows rows):
+    // gated: its gate rows and the matching up rows; down: its rows in two halves
+    const int range0 = nb * kColsPerWg;
     const int range1 = GATED ? p.n_out + range0 : range0 + kRangeRows;
 
     extern __shared__ uint4 lds[];
@@ -196,48 +221,56 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
     uint16_t *lds_z = lds_s + 2 * kRangeRows * NG;
     __shared__ int s_src[kBlockM];
 
-    // ---- 1. loads that need nothing but the tile: scale/zero ranges and the
-    // tile's row ids. Issued before the weight prefetch so waiting on them
-    // does not wait on weights.
+    // ---- 1. scale/zero of the workgroup's rows (two contiguous ranges of
+    // kRangeRows * NG fp16 each, 16-byte aligned) and the tile's row ids.
+    // Issued before the weight prefetch so that waiting for them does not
+    // wait for weights (loads complete in issue order).
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    const int range_dw = kRangeRows * NG / 2;      // dwords per range (NG * rows is even)
-    constexpr int kSzPerThread = 8;
-    uint32_t sv[kSzPerThread], zv[kSzPerThread];
-    const int sz_total = 2 * range_dw;
+    constexpr int kSzLoads = 8;                    // 16-byte loads per thread and array
+    const int range_seg = kRangeRows * NG / 8;     // 16-byte segments per range
+    const int sz_total = 2 * range_seg;
     auto sz_off = [&](int x) -> uint32_t {
         if (x >= sz_total)
             return kOutOfRange;
-        const int r = x >= range_dw;
-        return (uint32_t)((r ? range1 : range0) * NG) * 2u + (uint32_t)(x - r * range_dw) * 4u;
+        const int r = x >= range_seg;
+        return (uint32_t)((r ? range1 : range0) * NG) * 2u + (uint32_t)(x - r * range_seg) * 16u;
     };
+    uint4 sv[kSzLoads], zv[kSzLoads];
 #pragma unroll
-    for (int i = 0; i < kSzPerThread; ++i) {
+    for (int i = 0; i < kSzLoads; ++i) {
         const uint32_t off = sz_off(i * kThreads + tid);
-        sv[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-        zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+        sv[i] = load16(rs, off, 0);
+        zv[i] = load16(rz, off, 0);
     }
     int fid = 0;
-    if (GATED && tid < kBlockM)
+    if (tid < kBlockM)
         fid = p.sorted_ids[row0 + tid];            // row0 + tid < cap: always in the buffer
 
     // ---- 2. weight prefetch, D groups
-    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
-    uint32_t wvoff[kTilesPerWave];
-    int lds_row[kTilesPerWave];                    // this lane's row in the scale/zero ranges
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2),
+                                wave_live ? (uint32_t)p.n_w * (uint32_t)(K / 2) : 0u);
+    uint32_t wvoff[TPW];
+    int lds_row[TPW];                              // this lane's row in the scale/zero ranges
 #pragma unroll
-    for (int tt = 0; tt < kTilesPerWave; ++tt) {
-        const int in_range = GATED ? wave * 16 + lrow : wave * 32 + tt * 16 + lrow;
-        const int wr = (GATED ? (tt ? range1 : range0) : range0) + in_range;
-        wvoff[tt] = wave_live ? (uint32_t)wr * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8))
-                              : (uint32_t)(quarter * (G / 8));
-        lds_row[tt] = GATED ? tt * kRangeRows + in_range : in_range;
+    for (int tt = 0; tt < TPW; ++tt) {
+        int wr;
+        if constexpr (GATED) {
+            const int in_range = wave * kColsPerWave + (tt >> 1) * 16 + lrow;
+            wr = ((tt & 1) ? range1 : range0) + in_range;
+            lds_row[tt] = (tt & 1) * kRangeRows + in_range;
+        } else {
+            const int in_range = wave * kColsPerWave + tt * 16 + lrow;
+            wr = range0 + in_range;
+            lds_row[tt] = in_range;
+        }
+        wvoff[tt] = (uint32_t)wr * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8));
     }
-    Frag<G> bq[D][kTilesPerWave];
+    Frag<G> bq[D][TPW];
     auto prefetch = [&](int s, int gi) {      // group gi (clamped) into stage s
         gi = min(gi, NG - 1);
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt)
+        for (int tt = 0; tt < TPW; ++tt)
             bq[s][tt] = load_frag<G>(rq, wvoff[tt], (uint32_t)(gi * (G / 2)));
     };
 #pragma unroll
@@ -247,19 +280,19 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
 
     // ---- 3. scale/zero and row sources into LDS
     {
-        uint32_t *ls = reinterpret_cast<uint32_t *>(lds_s);
-        uint32_t *lz = reinterpret_cast<uint32_t *>(lds_z);
+        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
+        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
 #pragma unroll
-        for (int i = 0; i < kSzPerThread; ++i) {
+        for (int i = 0; i < kSzLoads; ++i) {
             const int x = i * kThreads + tid;
             if (x < sz_total) {
                 ls[x] = sv[i];
                 lz[x] = zv[i];
             }
         }
-        for (int x = kSzPerThread * kThreads + tid; x < sz_total; x += kThreads) {
-            ls[x] = __builtin_amdgcn_raw_buffer_load_b32(rs, sz_off(x), 0, 0);   // large NG only
-            lz[x] = __builtin_amdgcn_raw_buffer_load_b32(rz, sz_off(x), 0, 0);
+        for (int x = kSzLoads * kThreads + tid; x < sz_total; x += kThreads) {   // large NG only
+            ls[x] = load16(rs, sz_off(x), 0);
+            lz[x] = load16(rz, sz_off(x), 0);
         }
     }
     if (tid < kBlockM)
@@ -269,9 +302,9 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
     // ---- 4. activation staging (sources are already in the permuted K order)
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
     uint4 *lds_a = lds;
-    f32x4 acc[kTilesPerWave][2];
+    f32x4 acc[TPW][2];
 #pragma unroll
-    for (int tt = 0; tt < kTilesPerWave; ++tt)
+    for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
             acc[tt][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -280,16 +313,16 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
     const f16x2 k64 = {(_Float16)64.0f, (_Float16)64.0f};
 
     // group gi from stage s over NMS 16-row blocks, reading activations at
-    // 16-byte segment seg0 (+ lane offsets) of the LDS rows starting at abuf
+    // 16-byte segment seg0 (+ lane offsets) of the LDS rows starting at abuf.
     // A group past the last one (gi >= NG, in a padded trip) contributes
     // exactly nothing: its scale is taken as 0 and every index is clamped.
     auto group = [&](int s, const uint4 *abuf, int pitch, int seg0, int gi, auto nms_tag) {
         constexpr int NMS = decltype(nms_tag)::value;
-        f16x2 c1024[kTilesPerWave], c64[kTilesPerWave];
-        float scale[kTilesPerWave];
+        f16x2 c1024[TPW], c64[TPW];
+        float scale[TPW];
         const int gc = min(gi, NG - 1);
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt) {
+        for (int tt = 0; tt < TPW; ++tt) {
             const uint32_t zb = lds_z[lds_row[tt] * NG + gc];
             const f16x2 zz = as_h2(zb | (zb << 16));
             c1024[tt] = zz + k1024;          // fp16(1024 + z), exact for |z| <= 1024
@@ -297,25 +330,25 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
             const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
             scale[tt] = gi < NG ? sc : 0.0f;
         }
-        f32x4 part[kTilesPerWave][NMS];
+        f32x4 part[TPW][NMS];
 #pragma unroll
         for (int t = 0; t < kWords; ++t) {
-            f16x8 bop[kTilesPerWave];
+            f16x8 bop[TPW];
 #pragma unroll
-            for (int tt = 0; tt < kTilesPerWave; ++tt)
+            for (int tt = 0; tt < TPW; ++tt)
                 bop[tt] = dequant8(frag_word<G>(bq[s][tt], t), c1024[tt], c64[tt]);
             const int seg = seg0 + quarter * (G / 32) + t;   // this lane's 8 K positions
 #pragma unroll
             for (int ms = 0; ms < NMS; ++ms) {
                 const f16x8 aop = __builtin_bit_cast(f16x8, abuf[(ms * 16 + lrow) * pitch + seg]);
 #pragma unroll
-                for (int tt = 0; tt < kTilesPerWave; ++tt)
+                for (int tt = 0; tt < TPW; ++tt)
                     part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         aop, bop[tt], t == 0 ? zero4 : part[tt][ms], 0, 0, 0);
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < kTilesPerWave; ++tt)
+        for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
             for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
@@ -384,29 +417,29 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
         };
         load_chunk(0);
         store_chunk(0);                           // read only after the loop's first barrier
-        // Two chunks per trip so that every register stage index is static, and
-        // no branch inside a trip (an odd chunk count runs one padded chunk
-        // whose activations read as zero and whose groups have scale 0), so
-        // the wait counts the compiler derives stay exact. Per chunk: load the
+        // TRIP chunks per trip and no branch inside a trip (chunks past the
+        // end read activations as zero and their groups have scale 0), so the
+        // wait counts the compiler derives stay exact. Per chunk: load the
         // next activation chunk into registers, one barrier (this chunk is in
         // LDS, the other buffer is free), the chunk's groups each followed by
-        // the prefetch of the group two chunks ahead, then store the next chunk.
+        // the prefetch of the group kAhead chunks ahead, then store the next
+        // chunk.
         auto run = [&](auto nms_tag) {
-            for (int c0 = 0; c0 < NC; c0 += 2) {
+            for (int c0 = 0; c0 < NC; c0 += TRIP) {
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int c = c0 + half;
+                for (int j = 0; j < TRIP; ++j) {
+                    const int c = c0 + j;
                     load_chunk(c + 1);
                     __builtin_amdgcn_sched_barrier(0);
                     __syncthreads();
-                    const uint4 *abuf = lds_a + half * kBlockM * kChunkPitch;
+                    const uint4 *abuf = lds_a + (j & 1) * kBlockM * kChunkPitch;
 #pragma unroll
                     for (int cs = 0; cs < CG; ++cs) {
                         const int gi = c * CG + cs;
-                        group(half * CG + cs, abuf, kChunkPitch, cs * (G / 8), gi, nms_tag);
-                        prefetch(half * CG + cs, gi + D);
+                        group((j * CG + cs) % D, abuf, kChunkPitch, cs * (G / 8), gi, nms_tag);
+                        prefetch((j * CG + cs) % D, gi + D);
                     }
-                    store_chunk(half ^ 1);
+                    store_chunk((j & 1) ^ 1);
                 }
             }
         };
@@ -427,48 +460,51 @@ __attribute__((amdgpu_waves_per_eu(WAVES == 8 ? 4 : 2))) moe_gemm_kernel(GemmArg
             if (r >= valid)
                 continue;
             if constexpr (GATED) {
-                const int col = col_first + lrow;
-                const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
                 uint16_t *H = static_cast<uint16_t *>(p.out);
-                H[(size_t)(row0 + r) * p.n_out + permuted_col(col)] =
-                    __builtin_bit_cast(uint16_t, (_Float16)h);
+#pragma unroll
+                for (int pp = 0; pp < TPW / 2; ++pp) {
+                    const int col = col_first + pp * 16 + lrow;
+                    const float h = gelu_tanh(acc[2 * pp][ms][i]) * acc[2 * pp + 1][ms][i];
+                    H[(size_t)(row0 + r) * p.n_out + permuted_col(col)] =
+                        __builtin_bit_cast(uint16_t, (_Float16)h);
+                }
             } else {
                 const int f = p.sorted_ids[row0 + r];
                 float *Y = static_cast<float *>(p.out);
 #pragma unroll
-                for (int tt = 0; tt < kTilesPerWave; ++tt)
+                for (int tt = 0; tt < TPW; ++tt)
                     Y[(size_t)f * p.n_out + col_first + tt * 16 + lrow] = acc[tt][ms][i];
             }
         }
     }
 }
 
-// Shape of each launch: gate_up streams K = d in chunks with 4 waves per
-// workgroup; down stages its whole K = m once (when m <= kSingleK) and shares
-// it among 8 waves.
-template <bool GATED, bool SINGLE>
-struct Shape {
-    static constexpr int kWaves = GATED ? 4 : 8;
-};
+// Shapes in use. gate_up streams K = d in chunks; down stages its whole
+// K = m once when m <= kSingleK and shares it among 8 waves whose register
+// budget (4 waves per SIMD) lets two workgroups share a CU.
+using GateUpShape = Shape<4, 4, 128, 2, 2>;
+using DownSingleShape = Shape<8, 2, 0, 0, 4>;
+using DownChunkShape = Shape<4, 2, 512, 2, 2>;
 
-template <int G, bool GATED, bool SINGLE>
+template <int G, bool GATED, class S>
 size_t lds_bytes(int K)
 {
-    constexpr int W = Shape<GATED, SINGLE>::kWaves;
-    const size_t a = SINGLE ? (size_t)kBlockM * (K / 8 + 1) : (size_t)2 * kBlockM * kChunkPitch;
-    return sizeof(uint4) * a + 2 * sizeof(uint16_t) * 2 * (W * 16) * (size_t)(K / G);
+    const bool single = S::kChunkK == 0;
+    const size_t pitch = single ? (size_t)K / 8 + 1 : (size_t)S::kChunkK / 8 + 1;
+    const size_t a = single ? kBlockM * pitch : 2 * kBlockM * pitch;
+    const size_t range_rows = (size_t)S::kWaves * S::kTiles * 8;
+    return sizeof(uint4) * a + 2 * sizeof(uint16_t) * 2 * range_rows * (size_t)(K / G);
 }
 
-template <int G, bool GATED, bool SINGLE>
+template <int G, bool GATED, class S>
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 {
-    constexpr int W = Shape<GATED, SINGLE>::kWaves;
-    const int cols_per_wg = GATED ? W * 16 : W * 32;
+    constexpr int cols_per_wg = S::kWaves * (GATED ? S::kTiles / 2 : S::kTiles) * 16;
     const int nblocks = (a.n_out + cols_per_wg - 1) / cols_per_wg;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    const size_t lds = lds_bytes<G, GATED, SINGLE>(a.K);
-    auto kern = moe_gemm_kernel<G, GATED, W, SINGLE>;
+    const size_t lds = lds_bytes<G, GATED, S>(a.K);
+    auto kern = moe_gemm_kernel<G, GATED, S>;
     static size_t lds_allowed = 64 * 1024;   // raised once per instantiation when needed
     if (lds > lds_allowed) {
         hipError_t err = hipFuncSetAttribute((const void *)kern,
@@ -477,7 +513,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
             return err;
         lds_allowed = lds;
     }
-    kern<<<dim3(nblocks, a.max_tiles), dim3(W * 64), lds, stream>>>(a);
+    kern<<<dim3(nblocks, a.max_tiles), dim3(S::kWaves * 64), lds, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -486,25 +522,27 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 size_t gemm_lds_bytes(bool gated, int K, int g)
 {
     if (gated)
-        return g == 128 ? lds_bytes<128, true, false>(K) : lds_bytes<64, true, false>(K);
+        return g == 128 ? lds_bytes<128, true, GateUpShape>(K) : lds_bytes<64, true, GateUpShape>(K);
     if (K <= kSingleK)
-        return g == 128 ? lds_bytes<128, false, true>(K) : lds_bytes<64, false, true>(K);
-    return g == 128 ? lds_bytes<128, false, false>(K) : lds_bytes<64, false, false>(K);
+        return g == 128 ? lds_bytes<128, false, DownSingleShape>(K)
+                        : lds_bytes<64, false, DownSingleShape>(K);
+    return g == 128 ? lds_bytes<128, false, DownChunkShape>(K)
+                    : lds_bytes<64, false, DownChunkShape>(K);
 }
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
-    return g == 128 ? launch_gemm<128, true, false>(a, stream)
-                    : launch_gemm<64, true, false>(a, stream);
+    return g == 128 ? launch_gemm<128, true, GateUpShape>(a, stream)
+                    : launch_gemm<64, true, GateUpShape>(a, stream);
 }
 
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
 {
     if (a.K <= kSingleK)
-        return g == 128 ? launch_gemm<128, false, true>(a, stream)
-                        : launch_gemm<64, false, true>(a, stream);
-    return g == 128 ? launch_gemm<128, false, false>(a, stream)
-                    : launch_gemm<64, false, false>(a, stream);
+        return g == 128 ? launch_gemm<128, false, DownSingleShape>(a, stream)
+                        : launch_gemm<64, false, DownSingleShape>(a, stream);
+    return g == 128 ? launch_gemm<128, false, DownChunkShape>(a, stream)
+                    : launch_gemm<64, false, DownChunkShape>(a, stream);
 }
 
 }  // namespace dgw4
