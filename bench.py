@@ -30,6 +30,8 @@ HBM_PEAK_GBPS = 8000.0
 # with the measured machine"): 2.366 ms. As GB/s on this layer's algorithmic
 # bytes it is context from another machine, not a target.
 GB10_LAYER_MS = 2.366
+# One timed step in SAMPLE carries the five stage events (see main()).
+SAMPLE = 10
 
 
 def log(*a):
@@ -86,6 +88,9 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=30, help="distinct weight sets in rotation")
     ap.add_argument("--workload", default="stack", choices=["stack", "full", "skew", "wide"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
+                    help="only run a plain device copy of MIB MiB 5 times (the counter "
+                         "calibration kernel for HBM traffic) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -103,6 +108,15 @@ def main() -> int:
     dg.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[copy] 5 copies of {n} bytes")
+        return 0
     shape = CONFIGS[args.workload]
     L = args.layers if args.workload == "stack" else 1
     if args.workload != "stack":
@@ -140,8 +154,12 @@ def main() -> int:
     for i in range(args.warmup):
         step(i)
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    for e in evs:                       # create the HIP events outside the timed region
+    # Stage events on every SAMPLE-th step of the timed region: each recorded
+    # event adds a few microseconds of dispatch gap, so recording them on
+    # every step would inflate the step time they are meant to split.
+    sampled = list(range(0, K, SAMPLE))
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(5)] for i in sampled}
+    for e in evs.values():              # create the HIP events outside the timed region
         for x in e:
             x.record(stream)
     start = torch.cuda.Event(enable_timing=True)
@@ -149,18 +167,16 @@ def main() -> int:
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        step(i, evs[i])
+        step(i, evs.get(i))
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
 
-    stage_ms = np.zeros((K, 4))
-    for i in range(K):
-        for j in range(4):
-            stage_ms[i, j] = evs[i][j].elapsed_time(evs[i][j + 1])
+    stage_ms = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                         for i in sampled])
     moved = sum(layers[i % L]["bytes"]["layer"] for i in range(K))
-    gu_bytes = sum(layers[i % L]["bytes"]["gate_up"] for i in range(K))
-    dn_bytes = sum(layers[i % L]["bytes"]["down"] for i in range(K))
+    gu_bytes = sum(layers[i % L]["bytes"]["gate_up"] for i in sampled)
+    dn_bytes = sum(layers[i % L]["bytes"]["down"] for i in sampled)
     ms_per_step = total_ms / K
     gbps = moved / (total_ms * 1e-3) / 1e9
     stage_us = {n: round(float(stage_ms[:, j].mean() * 1e3), 2)

@@ -12,10 +12,11 @@
 //
 // gfx950 design
 // -------------
-// Grid (N-block, tile): tile = one 32-row block of the padded assignment list
-// (one expert), N-block = WAVES waves x 2 MFMA column tiles of 16 weight rows.
-// Tiles past the device-side total exit at once, so the grid is static and
-// the host never reads the routing.
+// Work item (N-block, tile): tile = one 32-row block of the padded
+// assignment list (one expert), N-block = the output columns of one
+// workgroup. Tiles past the device-side total exit at once, so the grid is
+// static and the host never reads the routing. Items are laid out so that
+// every N-block of a tile runs on the same XCD, back to back.
 //
 // Each wave streams its 32 weight rows once, straight from the canonical
 // packed layout: per group and column tile a lane loads g/8 bytes (16 bytes
@@ -62,6 +63,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kSingleK = 768;            // largest K staged at once (one loop-free pass)
+constexpr int kXcds = 8;                 // accelerator dies (each with its own L2) on MI355X
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // a voffset no buffer here reaches
 
 // Raw buffer resource over [base, base + bytes): reads past the end return 0.
@@ -184,8 +186,16 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
     constexpr int kRangeRows = WAVES * TPW * 8;    // rows of each scale/zero range
     constexpr int kChunkLoads = kBlockM * kChunkSeg / kThreads;
     static_assert(!GATED || TPW % 2 == 0, "gated tiles come in gate/up pairs");
-    const int nb = blockIdx.x;
-    const int tile = blockIdx.y;
+    // Workgroup -> (N-block, tile), XCD-aware: consecutive workgroups are
+    // dispatched to the XCDs in turn, so XCD x takes tiles x, x + 8, ... and
+    // runs all N-blocks of a tile back to back; the tile's activation rows
+    // then stay in that XCD's L2 while its N-blocks reuse them.
+    const int nblocks = (p.n_out + kColsPerWg - 1) / kColsPerWg;
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int nb = slot % nblocks;
+    const int tile = slot / nblocks * kXcds + xcd;
+    if (tile >= p.max_tiles)
+        return;
     const int total = *p.num_padded;
     if (tile * kBlockM >= total)
         return;
@@ -513,7 +523,8 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
             return err;
         lds_allowed = lds;
     }
-    kern<<<dim3(nblocks, a.max_tiles), dim3(S::kWaves * 64), lds, stream>>>(a);
+    const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
+    kern<<<dim3(tiles * nblocks), dim3(S::kWaves * 64), lds, stream>>>(a);
     return hipGetLastError();
 }
 
