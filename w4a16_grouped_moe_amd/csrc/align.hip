@@ -16,8 +16,9 @@
 //      starting points (in wave order) and carries a running cursor across
 //      rounds. The result is the ascending-flat-id order inside every expert,
 //      independent of timing;
-//   4. each expert writes its own pad entries and tile map entries; the tail
-//      of the buffers past the total is filled by all threads.
+//   4. each expert writes its own pad entries and tile map entries (and, for
+//      the forward, the tile descriptors {expert, valid rows}); the tail of
+//      the buffers past the total is filled by all threads.
 // Ids outside [0, E) are skipped everywhere.
 //
 // Workgroups 1.. (forward only) copy x into the permuted K order the GEMM
@@ -49,6 +50,7 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
                                                         int32_t *__restrict__ sorted_ids,
                                                         int32_t *__restrict__ tile_expert,
                                                         int32_t *__restrict__ num_padded,
+                                                        int2 *__restrict__ tile_info,
                                                         const uint4 *__restrict__ x,
                                                         uint4 *__restrict__ xp, long long x_segs)
 {
@@ -163,13 +165,19 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
     for (int e = tid; e < E; e += kThreads) {
         for (int p = s_off[e] + s_cnt[e]; p < s_off[e + 1]; ++p)
             sorted_ids[p] = A;
-        for (int t = s_off[e] / bm; t < s_off[e + 1] / bm; ++t)
+        for (int t = s_off[e] / bm; t < s_off[e + 1] / bm; ++t) {
             tile_expert[t] = e;
+            if (tile_info)
+                tile_info[t] = make_int2(e, min(bm, s_cnt[e] - (t * bm - s_off[e])));
+        }
     }
     for (int p = total + tid; p < cap; p += kThreads)
         sorted_ids[p] = A;
-    for (int t = total / bm + tid; t < cap / bm; t += kThreads)
+    for (int t = total / bm + tid; t < cap / bm; t += kThreads) {
         tile_expert[t] = -1;
+        if (tile_info)
+            tile_info[t] = make_int2(-1, 0);
+    }
 }
 
 }  // namespace
@@ -182,13 +190,13 @@ hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long
                         int32_t *tile_expert, int32_t *num_padded, hipStream_t stream)
 {
     return launch_prep(topk_ids, A, E, block_m, cap, counts, offsets, sorted_ids, tile_expert,
-                       num_padded, nullptr, nullptr, 0, stream);
+                       num_padded, nullptr, nullptr, nullptr, 0, stream);
 }
 
 hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                        int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
-                       int32_t *tile_expert, int32_t *num_padded, const uint16_t *x,
-                       uint16_t *xp, long long x_elems, hipStream_t stream)
+                       int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
+                       const uint16_t *x, uint16_t *xp, long long x_elems, hipStream_t stream)
 {
     const long long segs = x_elems / 8;
     const long long want = (segs + kThreads - 1) / kThreads;
@@ -210,11 +218,11 @@ hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long 
         }
         kern<<<grid, dim3(kThreads), lds, stream>>>(topk_ids, A, E, block_m, (int)cap, counts,
                                                     offsets, sorted_ids, tile_expert, num_padded,
-                                                    x4, xp4, segs);
+                                                    tile_info, x4, xp4, segs);
     } else {
         align_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(
             topk_ids, A, E, block_m, (int)cap, counts, offsets, sorted_ids, tile_expert,
-            num_padded, x4, xp4, segs);
+            num_padded, tile_info, x4, xp4, segs);
     }
     return hipGetLastError();
 }

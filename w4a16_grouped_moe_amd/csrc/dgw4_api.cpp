@@ -34,7 +34,7 @@ int from_hip(hipError_t e)
 // the gated intermediate H (fp16, one row per padded assignment) and the
 // per-assignment expert outputs Y (fp32, one row per flat assignment id).
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, sorted_ids, xp, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, xp, h, y, total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap)
@@ -50,6 +50,7 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
+    L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.xp = take(sizeof(uint16_t) * (size_t)T * (size_t)d);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
@@ -183,6 +184,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int32_t *offsets = reinterpret_cast<int32_t *>(ws + L.offsets);
     int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
+    int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
     uint16_t *xp = reinterpret_cast<uint16_t *>(ws + L.xp);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
@@ -191,8 +193,8 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     hipError_t err = mark(0);
     if (err == hipSuccess)
         err = dgw4::launch_prep(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
-                                offsets, sorted_ids, tile_expert, num_padded, x, xp,
-                                (long long)T * d, st);
+                                offsets, sorted_ids, tile_expert, num_padded, tile_info, x,
+                                xp, (long long)T * d, st);
     if (err == hipSuccess)
         err = mark(1);
     if (err != hipSuccess)
@@ -200,10 +202,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
 
     dgw4::GemmArgs g{};
     g.sorted_ids = sorted_ids;
-    g.tile_expert = tile_expert;
-    g.counts = counts;
-    g.offsets = offsets;
-    g.num_padded = num_padded;
+    g.tile_info = tile_info;
     g.topk = topk;
     g.A = (int)A;
     g.max_tiles = (int)(cap / dgw4::kBlockM);

@@ -24,11 +24,13 @@ hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long
                         int32_t *tile_expert, int32_t *num_padded, hipStream_t stream);
 
 // The alignment plus, in extra workgroups of the same launch, a copy of x
-// [x_elems fp16] into xp with each 8 values in the GEMM's K order.
+// [x_elems fp16] into xp with each 8 values in the GEMM's K order, and the
+// per-tile descriptors the GEMMs read: tile_info[j] = {expert, rows of the
+// tile that hold assignments} for live tiles, {-1, 0} past the total.
 hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                        int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
-                       int32_t *tile_expert, int32_t *num_padded, const uint16_t *x,
-                       uint16_t *xp, long long x_elems, hipStream_t stream);
+                       int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
+                       const uint16_t *x, uint16_t *xp, long long x_elems, hipStream_t stream);
 
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
@@ -37,10 +39,7 @@ struct GemmArgs {
     const uint16_t *a_src;      // gate_up: x [T, d]; down: H [cap, m] (both permuted per 8)
     int a_rows;                 // rows of a_src (T or cap)
     const int32_t *sorted_ids;  // [cap]
-    const int32_t *tile_expert; // [cap / kBlockM]
-    const int32_t *counts;      // [E]
-    const int32_t *offsets;     // [E + 1]
-    const int32_t *num_padded;  // [1]
+    const int2 *tile_info;      // [cap / kBlockM]: {expert or -1, valid rows}
     const uint8_t *q;           // packed weights [E, n_w, K/2]
     const uint16_t *s;          // [E, n_w, K/g]
     const uint16_t *z;          // [E, n_w, K/g]

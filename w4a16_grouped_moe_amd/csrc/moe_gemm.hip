@@ -130,11 +130,17 @@ __device__ inline f16x8 dequant8(uint32_t w, f16x2 c1024, f16x2 c64)
     return r;
 }
 
+// GELU, tanh form: 0.5 v (1 + tanh(u)) with u = sqrt(2/pi) (v + 0.044715 v^3).
+// Since 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), this is v / (1 + exp(-2u)):
+// one hardware exp2 and one reciprocal (each within about 1 ulp) instead of a
+// library tanh. Both limits hold: exp2 -> +inf gives 0, exp2 -> 0 gives v.
 __device__ inline float gelu_tanh(float v)
 {
     const float k0 = 0.7978845608028654f;   // sqrt(2/pi)
     const float k1 = 0.044715f;
-    return 0.5f * v * (1.0f + tanhf(k0 * (v + k1 * v * v * v)));
+    const float m2log2e = -2.8853900817779268f;   // -2 log2(e)
+    const float u = k0 * (v + k1 * v * v * v);
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
 }
 
 // Position of column c inside its row when a row is stored permuted per 8
@@ -196,12 +202,12 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
     const int tile = slot / nblocks * kXcds + xcd;
     if (tile >= p.max_tiles)
         return;
-    const int total = *p.num_padded;
-    if (tile * kBlockM >= total)
+    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    if (info.x < 0)
         return;
-    const int e = p.tile_expert[tile];
+    const int e = info.x;
+    const int valid = info.y;
     const int row0 = tile * kBlockM;               // first padded row of this tile
-    const int valid = min(kBlockM, p.counts[e] - (row0 - p.offsets[e]));
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
