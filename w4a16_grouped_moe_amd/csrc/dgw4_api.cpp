@@ -34,7 +34,7 @@ int from_hip(hipError_t e)
 // the gated intermediate H (fp16, one row per padded assignment) and the
 // per-assignment expert outputs Y (fp32, one row per flat assignment id).
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, xp, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap)
@@ -52,7 +52,6 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
-    L.xp = take(sizeof(uint16_t) * (size_t)T * (size_t)d);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take(sizeof(float) * (size_t)A * (size_t)d);
     L.total = off;
@@ -119,7 +118,7 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
     if (cap == 0)
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_align(topk_ids, T * topk, E, block_m, (long long)cap, counts,
-                                       offsets, sorted_ids, tile_expert, num_padded,
+                                       offsets, sorted_ids, tile_expert, num_padded, nullptr,
                                        (hipStream_t)stream));
 }
 
@@ -186,15 +185,13 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
     int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
-    uint16_t *xp = reinterpret_cast<uint16_t *>(ws + L.xp);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     float *y = reinterpret_cast<float *>(ws + L.y);
 
     hipError_t err = mark(0);
     if (err == hipSuccess)
-        err = dgw4::launch_prep(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
-                                offsets, sorted_ids, tile_expert, num_padded, tile_info, x,
-                                xp, (long long)T * d, st);
+        err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
+                                 offsets, sorted_ids, tile_expert, num_padded, tile_info, st);
     if (err == hipSuccess)
         err = mark(1);
     if (err != hipSuccess)
@@ -207,7 +204,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     g.A = (int)A;
     g.max_tiles = (int)(cap / dgw4::kBlockM);
 
-    g.a_src = xp;
+    g.a_src = x;
     g.a_rows = T;
     g.q = gu_q;
     g.s = gu_s;

@@ -19,24 +19,19 @@ constexpr int kMaxExperts = 1024;
 hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t *q,
                                uint16_t *s, uint16_t *z, hipStream_t stream);
 
+// Alignment of the flat assignment ids to experts (one workgroup per
+// expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
+// the tile that hold assignments} for live tiles, {-1, 0} past the total.
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
-                        int32_t *tile_expert, int32_t *num_padded, hipStream_t stream);
-
-// The alignment plus, in extra workgroups of the same launch, a copy of x
-// [x_elems fp16] into xp with each 8 values in the GEMM's K order, and the
-// per-tile descriptors the GEMMs read: tile_info[j] = {expert, rows of the
-// tile that hold assignments} for live tiles, {-1, 0} past the total.
-hipError_t launch_prep(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
-                       int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
-                       int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
-                       const uint16_t *x, uint16_t *xp, long long x_elems, hipStream_t stream);
+                        int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
+                        hipStream_t stream);
 
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
 
 struct GemmArgs {
-    const uint16_t *a_src;      // gate_up: x [T, d]; down: H [cap, m] (both permuted per 8)
+    const uint16_t *a_src;      // gate_up: x [T, d] (natural order); down: H [cap, m] (permuted per 8)
     int a_rows;                 // rows of a_src (T or cap)
     const int32_t *sorted_ids;  // [cap]
     const int2 *tile_info;      // [cap / kBlockM]: {expert or -1, valid rows}
@@ -50,6 +45,8 @@ struct GemmArgs {
     int A;                      // T * topk; also the pad sentinel in sorted_ids
     int max_tiles;              // cap / kBlockM
     void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp32 [A, d]
+    const void *asum;           // per row of a_src and 64 columns: {sum_k M_k a_k, sum_k a_k} fp32
+    void *out_sum;              // gate_up: the same sums of the H rows it writes [cap, m / 64]
 };
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);

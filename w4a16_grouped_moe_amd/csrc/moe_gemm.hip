@@ -32,8 +32,8 @@
 // subtract of (1024 + z) or (64 + z) leaves the exact integers q - z. The
 // MFMA B operand therefore holds K positions in the order [0,4,1,5,2,6,3,7]
 // within each 8. A contraction is unchanged by the same permutation on both
-// operands, so the activations are consumed in that same order: x is
-// permuted once per forward by the preparation kernel and H is written
+// operands, so the activations are consumed in that same order: gate_up
+// permutes each 8 values of x as it stages them in LDS, and H is written
 // permuted by gate_up's epilogue. No weight preshuffle is needed.
 //
 // v_mfma_f32_16x16x32_f16 accumulates one group (g/32 MFMAs) into a fresh
@@ -141,6 +141,18 @@ __device__ inline float gelu_tanh(float v)
     const float m2log2e = -2.8853900817779268f;   // -2 log2(e)
     const float u = k0 * (v + k1 * v * v * v);
     return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(m2log2e * u));
+}
+
+// 8 consecutive fp16 values (K order 0..7) -> the same values in the
+// dequantised weights' order [0,4,1,5,2,6,3,7].
+__device__ inline uint4 permute8(uint4 v)
+{
+    uint4 o;
+    o.x = (v.x & 0xFFFFu) | (v.z << 16);
+    o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);
+    o.z = (v.y & 0xFFFFu) | (v.w << 16);
+    o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);
+    return o;
 }
 
 // Position of column c inside its row when a row is stored permuted per 8
@@ -429,7 +441,7 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
 #pragma unroll
             for (int i = 0; i < kChunkLoads; ++i)
                 lds_a[buf * kBlockM * kChunkPitch + (arow0 + i * kRowStep) * kChunkPitch + aseg] =
-                    xr[i];
+                    GATED ? permute8(xr[i]) : xr[i];
         };
         load_chunk(0);
         store_chunk(0);                           // read only after the loop's first barrier
