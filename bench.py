@@ -221,7 +221,7 @@ def main() -> int:
         "bytes_per_layer": layers[0]["bytes"]["layer"],
         "stage_us": stage_us,
         "roofline": {
-            "kernel": "moe_gemm_kernel<128, gated> (gate_up + GELU(tanh) gate)",
+            "kernel": "gate_up_kernel<128> (gate_up + GELU(tanh) gate)",
             "bound": "hbm",
             "achieved": round(gu_gbps, 1),
             "peak": HBM_PEAK_GBPS,

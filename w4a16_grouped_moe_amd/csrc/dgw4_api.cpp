@@ -11,8 +11,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
-// LDS of one CU; a GEMM workgroup must fit in half of it so that two can run.
-constexpr size_t kMaxGemmLds = 80 * 1024;
+// LDS of one CU (160 KB); a GEMM workgroup must fit in it.
+constexpr size_t kMaxGemmLds = 160 * 1024;
 
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -150,7 +150,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     if (cap == 0 || A > INT_MAX)
         return DGW4_ERR_INVALID_ARG;
     if (dgw4::gemm_lds_bytes(true, d, gu_g) > kMaxGemmLds ||
-        dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds)
+        dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds || m > dgw4::down_max_k())
         return DGW4_ERR_UNSUPPORTED;
     // the GEMMs address x, H and one expert's packed weights with 32-bit offsets
     if ((long long)T * d * 2 >= (1LL << 31) || (long long)cap * m * 2 >= (1LL << 31) ||

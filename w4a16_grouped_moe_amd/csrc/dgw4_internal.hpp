@@ -30,6 +30,9 @@ hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
 
+// Largest contraction width (m) the down GEMM supports.
+int down_max_k();
+
 struct GemmArgs {
     const uint16_t *a_src;      // gate_up: x [T, d] (natural order); down: H [cap, m] (permuted per 8)
     int a_rows;                 // rows of a_src (T or cap)
@@ -45,8 +48,6 @@ struct GemmArgs {
     int A;                      // T * topk; also the pad sentinel in sorted_ids
     int max_tiles;              // cap / kBlockM
     void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp32 [A, d]
-    const void *asum;           // per row of a_src and 64 columns: {sum_k M_k a_k, sum_k a_k} fp32
-    void *out_sum;              // gate_up: the same sums of the H rows it writes [cap, m / 64]
 };
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);

@@ -5,54 +5,56 @@
 // expert; the activation is folded into the first GEMM's epilogue) and
 // "W4A16" (the GEMM reads packed nibbles and dequantises inline); the model
 // card, "Checkpoint format" (w = (q - z) * s, one scale/zero per group along
-// K, byte j = q[2j] | q[2j+1] << 4; the group size matches the K step so one
-// scale and zero serve a whole K chunk); and the Part 2 blog, "Quantisation
-// alone leaves a sparse execution problem" and "The final best W4 MoE
-// kernel" (assignments sorted by expert and padded to 32-row blocks).
+// K, byte j = q[2j] | q[2j+1] << 4); and the Part 2 blog, "Quantisation alone
+// leaves a sparse execution problem" and "The final best W4 MoE kernel"
+// (assignments sorted by expert and padded to 32-row blocks).
 //
 // gfx950 design
 // -------------
-// Work item (N-block, tile): tile = one 32-row block of the padded
-// assignment list (one expert), N-block = the output columns of one
-// workgroup. Tiles past the device-side total exit at once, so the grid is
-// static and the host never reads the routing. Items are laid out so that
-// every N-block of a tile runs on the same XCD, back to back.
+// Both GEMMs stream the packed weights straight from the canonical layout.
+// A lane (row = lane % 16, quarter = lane / 16) loads g/8 bytes (16 for
+// g = 128, 8 for g = 64) of one weight row per group, so the four quarters
+// cover one whole group of 16 rows. Dequantisation builds exact fp16
+// integers in registers: for a 32-bit word of nibbles n0..n7,
+// (w & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + n0, 1024 + n4) and
+// (w & 0x00F000F0) | 0x54005400 is (64 + n1, 64 + n5); the same on w >> 8
+// gives n2/n6 and n3/n7, and one packed fp16 subtract of (1024 + z) or
+// (64 + z) leaves q - z exactly. The MFMA operand therefore holds K in the
+// order [0,4,1,5,2,6,3,7] per 8; the activations are used in the same order
+// (gate_up permutes x as it stages it, H is written permuted), which leaves
+// the contraction unchanged and needs no weight preshuffle.
+// v_mfma_f32_16x16x32_f16 accumulates one group into a fresh fp32 partial and
+// the group's scale is applied once per output in fp32 (acc += s * partial),
+// so no weight is ever rounded by its scale.
 //
-// Each wave streams its 32 weight rows once, straight from the canonical
-// packed layout: per group and column tile a lane loads g/8 bytes (16 bytes
-// for g=128, 8 for g=64) of one weight row with a buffer load whose group
-// offset is scalar; the four lane groups of 16 cover one whole group of that
-// row. D groups are in flight per wave; they stay in flight across the
-// workgroup barriers (the barrier waits only for LDS traffic).
+// Loads complete in issue order, and the compiler's wait counting is exact
+// only in straight-line code without a vector store in flight: a loop back
+// edge, or a store issued while loads are pending, turns waits into waits for
+// the whole queue. So the step loops are fully unrolled for the layer's
+// shapes (K = 2816 and 704; other shapes take a generic loop), every wait is
+// for data issued a fixed number of steps earlier, and down keeps its outputs
+// in registers until its last tile.
 //
-// Dequantisation builds exact fp16 integers in registers: for a 32-bit word
-// holding nibbles n0..n7, (w & 0x000F000F) | 0x64006400 is the fp16 pair
-// (1024 + n0, 1024 + n4) and (w & 0x00F000F0) | 0x54005400 is (64 + n1,
-// 64 + n5); the same on w >> 8 gives n2/n6 and n3/n7. One packed fp16
-// subtract of (1024 + z) or (64 + z) leaves the exact integers q - z. The
-// MFMA B operand therefore holds K positions in the order [0,4,1,5,2,6,3,7]
-// within each 8. A contraction is unchanged by the same permutation on both
-// operands, so the activations are consumed in that same order: gate_up
-// permutes each 8 values of x as it stages them in LDS, and H is written
-// permuted by gate_up's epilogue. No weight preshuffle is needed.
+// gate_up: workgroup = (32-row tile, 128 output columns), 8 waves, each wave
+// one 16-column gate tile and the matching up tile. K is walked in steps of
+// one 128-byte line of every weight row (256 K = two g=128 groups); the
+// weights and the activation slice of a step are loaded P = 2 steps ahead,
+// together, and the slice goes through a double-buffered LDS stage with one
+// barrier per step. Epilogue: gelu_tanh(gate) * up in fp32, H in fp16.
 //
-// v_mfma_f32_16x16x32_f16 accumulates one group (g/32 MFMAs) into a fresh
-// fp32 partial; the group's scale is applied once per output in fp32
-// (acc += s * partial). The scale never touches an fp16 weight, so the only
-// rounding is the fp32 accumulation.
+// down: workgroup = (32-row tile, part of 704 output columns), 4 waves. The
+// tile's activations (all of K) and the part's scales/zero points are staged
+// in LDS once; each wave then streams its 11 16-row weight tiles (all of K,
+// P = 2 tiles ahead) without any barrier. The MFMA takes the weights as its
+// row operand, so a lane ends with four consecutive output columns of one
+// assignment row: one 16-byte store of fp32 Y per row and tile, at the
+// assignment's flat slot t * topk + k.
 //
-// Activations: the tile's 32 rows are staged through LDS, either in K chunks
-// of 512 (double-buffered, loaded into registers one chunk ahead; gate_up)
-// or the whole K at once (down, K = m). Scale and zero point of the
-// workgroup's rows are copied into LDS once, as contiguous row ranges.
-//
-// Epilogues: gate_up computes gelu_tanh(gate) * up in fp32 and writes H in
-// fp16 at the tile's padded row (permuted per 8 columns, see above); down
-// writes fp32 Y at the assignment's flat slot t * topk + k, which the combine
-// reads in ascending k.
+// Both: tiles past the device-side total exit at once (static grid, no host
+// readback); the work items of one tile run back to back on one XCD so that
+// its activation rows stay in that XCD's L2; tiles with at most 16 valid rows
+// run one 16-row MFMA block instead of two.
 #include "dgw4_internal.hpp"
-
-#include <type_traits>
 
 namespace dgw4 {
 namespace {
@@ -62,9 +64,8 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int kSingleK = 768;            // largest K staged at once (one loop-free pass)
-constexpr int kXcds = 8;                 // accelerator dies (each with its own L2) on MI355X
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;    // a voffset no buffer here reaches
+constexpr int kXcds = 8;                          // accelerator dies (each with its own L2) on MI355X
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;     // a voffset no buffer here reaches
 
 // Raw buffer resource over [base, base + bytes): reads past the end return 0.
 __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -108,7 +109,8 @@ __device__ inline uint32_t frag_word(const Frag<G> &f, int t)
 __device__ inline f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
 // (w & mask) | magic in one v_and_or_b32 (gfx9 VOP3 takes no literal, so the
-// compiler would otherwise split it). The result only feeds ordinary VALU.
+// compiler would otherwise split it). The result only feeds ordinary VALU
+// (the packed subtract below), whose hazards the compiler tracks.
 __device__ inline uint32_t and_or(uint32_t w, uint32_t mask, uint32_t magic)
 {
     uint32_t r;
@@ -128,6 +130,14 @@ __device__ inline f16x8 dequant8(uint32_t w, f16x2 c1024, f16x2 c64)
     r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
     r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
     return r;
+}
+
+// fp16(1024 + z) and fp16(64 + z) as packed pairs; exact for -2033 <= z <= 1024
+__device__ inline void zero_point_consts(uint32_t zbits, f16x2 &c1024, f16x2 &c64)
+{
+    const f16x2 zz = as_h2(zbits | (zbits << 16));
+    c1024 = zz + f16x2{(_Float16)1024.0f, (_Float16)1024.0f};
+    c64 = zz + f16x2{(_Float16)64.0f, (_Float16)64.0f};
 }
 
 // GELU, tanh form: 0.5 v (1 + tanh(u)) with u = sqrt(2/pi) (v + 0.044715 v^3).
@@ -163,63 +173,44 @@ __device__ inline int permuted_col(int c)
     return (c & ~7) | ((j & 3) << 1) | (j >> 2);
 }
 
-// Launch shape of one GEMM kernel instantiation.
-//   kWaves    waves per workgroup
-//   kTiles    MFMA column tiles (16 weight rows each) per wave; gated: gate and
-//             up tiles alternate (tile 2p = gate rows, 2p + 1 = the matching
-//             up rows), so a wave owns kTiles / 2 * 16 output columns
-//   kChunkK   activation K per LDS chunk (0: the whole K staged at once)
-//   kAhead    activation chunks of weight groups kept in flight per wave
-//   kWpe      waves per SIMD the register budget is sized for
-template <int W, int T, int CK, int AH, int WPE>
-struct Shape {
+// ===========================================================================
+// gate_up
+//   kWaves  waves per workgroup
+//   kTiles  MFMA column tiles (16 weight rows each) per wave: gate and up
+//           alternate (tile 2p = gate rows, 2p + 1 = the matching up rows)
+//   kAhead  line steps (256 K) in flight per wave
+//   kWpe    waves per SIMD the register budget is sized for
+template <int W, int T, int P, int WPE>
+struct GuShape {
     static constexpr int kWaves = W;
     static constexpr int kTiles = T;
-    static constexpr int kChunkK = CK;
-    static constexpr int kAhead = AH;
+    static constexpr int kAhead = P;
     static constexpr int kWpe = WPE;
 };
+using GateUpShape = GuShape<8, 2, 2, 4>;
+constexpr int kGuSteps = 11;        // line steps of K = 2816, the layer's hidden size
+constexpr int kStepSeg = 32;        // 16-byte activation segments per row and step
+constexpr int kStepPitch = kStepSeg + 1;   // +16 B per row: 16 rows at one segment hit 16 bank groups
 
-template <int G, bool GATED, class S>
-__global__ void __launch_bounds__(S::kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
+// NSC > 0: the step count is a compile-time constant and the K loop is fully
+// unrolled; NSC = 0: a generic loop over ceil(K / 256) steps.
+template <int G, class S, int NMS, int NSC>
+__device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid, int row0, int nb)
 {
     constexpr int WAVES = S::kWaves;
     constexpr int TPW = S::kTiles;
-    constexpr bool SINGLE = S::kChunkK == 0;
+    constexpr int P = S::kAhead;
     constexpr int kThreads = WAVES * 64;
-    constexpr int kWords = G / 32;                 // MFMA K steps per group = words per fragment
-    constexpr int kChunkK = SINGLE ? G : S::kChunkK;
-    constexpr int kChunkSeg = kChunkK / 8;         // 16-byte segments per row and chunk
-    constexpr int kChunkPitch = kChunkSeg + 1;     // +16 B per row: spreads LDS banks
-    constexpr int CG = kChunkK / G;                // groups per activation chunk
-    // weight groups in flight per wave: all of K when staged at once, else
-    // kAhead chunks
-    constexpr int D = SINGLE ? kSingleK / G : S::kAhead * CG;
-    // chunks per loop trip: register stages and the two LDS buffers both
-    // repeat with it, so every index is static inside a trip
-    constexpr int TRIP = S::kAhead % 2 == 0 ? S::kAhead : 2 * S::kAhead;
-    constexpr int kColsPerWave = GATED ? TPW / 2 * 16 : TPW * 16;
+    constexpr int SG = 256 / G;                   // groups per line step
+    constexpr int kWords = G / 32;
+    constexpr int kColsPerWave = TPW / 2 * 16;
     constexpr int kColsPerWg = WAVES * kColsPerWave;
-    constexpr int kRangeRows = WAVES * TPW * 8;    // rows of each scale/zero range
-    constexpr int kChunkLoads = kBlockM * kChunkSeg / kThreads;
-    static_assert(!GATED || TPW % 2 == 0, "gated tiles come in gate/up pairs");
-    // Workgroup -> (N-block, tile), XCD-aware: consecutive workgroups are
-    // dispatched to the XCDs in turn, so XCD x takes tiles x, x + 8, ... and
-    // runs all N-blocks of a tile back to back; the tile's activation rows
-    // then stay in that XCD's L2 while its N-blocks reuse them.
-    const int nblocks = (p.n_out + kColsPerWg - 1) / kColsPerWg;
-    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    const int nb = slot % nblocks;
-    const int tile = slot / nblocks * kXcds + xcd;
-    if (tile >= p.max_tiles)
-        return;
-    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
-    if (info.x < 0)
-        return;
-    const int e = info.x;
-    const int valid = info.y;
-    const int row0 = tile * kBlockM;               // first padded row of this tile
+    constexpr int kRangeRows = kColsPerWg;        // gate rows (and up rows) of the workgroup
+    constexpr int kRows = NMS * 16;               // activation rows staged
+    constexpr int XLD = kRows * kStepSeg / kThreads;
+    static_assert(kRows * kStepSeg % kThreads == 0 && kThreads % kStepSeg == 0, "activation split");
+    static_assert(TPW % 2 == 0, "gate/up tiles come in pairs");
+    constexpr int TRIP = NSC > 0 ? NSC : (P % 2 == 0 ? P : 2 * P);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -228,41 +219,34 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
     const int quarter = lane >> 4;
     const int K = p.K;
     const int NG = K / G;
+    const int NS = NSC > 0 ? NSC : (K + 255) / 256;
+    const int n_out = p.n_out;
     const size_t wexp = (size_t)e * p.n_w;
-
-    // columns owned by this wave. A wave past the edge (n_out is a multiple
-    // of its width) runs the same code on an empty weight buffer: its loads
-    // return zeros without touching memory, and it stores nothing.
+    // a wave past the last column (n_out is a multiple of 16) loads no
+    // weights, skips the math and stores nothing; it still stages activations
     const int col_first = nb * kColsPerWg + wave * kColsPerWave;
-    const bool wave_live = col_first < p.n_out;
-    // the two scale/zero row ranges of this workgroup (each kRangeRows rows):
-    // gated: its gate rows and the matching up rows; down: its rows in two halves
-    const int range0 = nb * kColsPerWg;
-    const int range1 = GATED ? p.n_out + range0 : range0 + kRangeRows;
+    const bool wave_live = col_first < n_out;
+    const int range0 = nb * kColsPerWg;           // gate rows; up rows start at n_out + range0
 
     extern __shared__ uint4 lds[];
-    // [A buffers][scale][zero]: A is [kBlockM][pitch] uint4, scale/zero are
-    // [2 * kRangeRows][NG] fp16
-    const int a_pitch = SINGLE ? K / 8 + 1 : kChunkPitch;
-    const int a_entries = SINGLE ? kBlockM * a_pitch : 2 * kBlockM * kChunkPitch;
-    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + a_entries);
+    uint4 *lds_x = lds;                                             // [2][32][kStepPitch]
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kBlockM * kStepPitch);   // [2 kRangeRows][NG]
     uint16_t *lds_z = lds_s + 2 * kRangeRows * NG;
     __shared__ int s_src[kBlockM];
 
-    // ---- 1. scale/zero of the workgroup's rows (two contiguous ranges of
-    // kRangeRows * NG fp16 each, 16-byte aligned) and the tile's row ids.
-    // Issued before the weight prefetch so that waiting for them does not
-    // wait for weights (loads complete in issue order).
+    // ---- 1. scale/zero loads (two contiguous row ranges), row ids, and the
+    // weights of the first P steps. Scale/zero are issued first, so waiting
+    // for them does not wait for weights.
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    constexpr int kSzLoads = 8;                    // 16-byte loads per thread and array
+    constexpr int kSzLoads = 2;
     const int range_seg = kRangeRows * NG / 8;     // 16-byte segments per range
     const int sz_total = 2 * range_seg;
     auto sz_off = [&](int x) -> uint32_t {
         if (x >= sz_total)
             return kOutOfRange;
         const int r = x >= range_seg;
-        return (uint32_t)((r ? range1 : range0) * NG) * 2u + (uint32_t)(x - r * range_seg) * 16u;
+        return (uint32_t)(((r ? n_out : 0) + range0) * NG) * 2u + (uint32_t)(x - r * range_seg) * 16u;
     };
     uint4 sv[kSzLoads], zv[kSzLoads];
 #pragma unroll
@@ -273,40 +257,36 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
     }
     int fid = 0;
     if (tid < kBlockM)
-        fid = p.sorted_ids[row0 + tid];            // row0 + tid < cap: always in the buffer
+        fid = p.sorted_ids[row0 + tid];           // row0 + tid < cap: always in the buffer
 
-    // ---- 2. weight prefetch, D groups
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2),
                                 wave_live ? (uint32_t)p.n_w * (uint32_t)(K / 2) : 0u);
     uint32_t wvoff[TPW];
     int lds_row[TPW];                              // this lane's row in the scale/zero ranges
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-        int wr;
-        if constexpr (GATED) {
-            const int in_range = wave * kColsPerWave + (tt >> 1) * 16 + lrow;
-            wr = ((tt & 1) ? range1 : range0) + in_range;
-            lds_row[tt] = (tt & 1) * kRangeRows + in_range;
-        } else {
-            const int in_range = wave * kColsPerWave + tt * 16 + lrow;
-            wr = range0 + in_range;
-            lds_row[tt] = in_range;
-        }
+        const int in_range = wave * kColsPerWave + (tt >> 1) * 16 + lrow;
+        const int wr = ((tt & 1) ? n_out : 0) + range0 + in_range;
+        lds_row[tt] = (tt & 1) * kRangeRows + in_range;
         wvoff[tt] = (uint32_t)wr * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8));
     }
-    Frag<G> bq[D][TPW];
-    auto prefetch = [&](int s, int gi) {      // group gi (clamped) into stage s
-        gi = min(gi, NG - 1);
+    Frag<G> bq[P][TPW][SG];
+    auto issue_w = [&](int st, int s) {           // step s into register stage st
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt)
-            bq[s][tt] = load_frag<G>(rq, wvoff[tt], (uint32_t)(gi * (G / 2)));
+#pragma unroll
+            for (int h = 0; h < SG; ++h) {
+                const int gi = s * SG + h;
+                bq[st][tt][h] = load_frag<G>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
+                                             (uint32_t)(s * 128 + h * (G / 2)));
+            }
     };
 #pragma unroll
-    for (int s = 0; s < D; ++s)
-        prefetch(s, s);
+    for (int s = 0; s < P; ++s)
+        issue_w(s, s);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. scale/zero and row sources into LDS
+    // ---- 2. scale/zero and row sources into LDS
     {
         uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
         uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
@@ -318,231 +298,458 @@ __attribute__((amdgpu_waves_per_eu(S::kWpe))) moe_gemm_kernel(GemmArgs p)
                 lz[x] = zv[i];
             }
         }
-        for (int x = kSzLoads * kThreads + tid; x < sz_total; x += kThreads) {   // large NG only
+        for (int x = kSzLoads * kThreads + tid; x < sz_total; x += kThreads) {   // large K only
             ls[x] = load16(rs, sz_off(x), 0);
             lz[x] = load16(rz, sz_off(x), 0);
         }
     }
     if (tid < kBlockM)
-        s_src[tid] = tid < valid ? (GATED ? fid / p.topk : row0 + tid) : -1;
+        s_src[tid] = tid < valid ? fid / p.topk : -1;
     __syncthreads();
 
-    // ---- 4. activation staging (sources are already in the permuted K order)
+    // ---- 3. activation slices: thread -> (row, 16-byte segment) of a step,
+    // the segment the same in every row it loads; the first P steps now
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
-    uint4 *lds_a = lds;
-    f32x4 acc[TPW][2];
+    const int xseg = tid % kStepSeg;
+    uint32_t xoff[XLD];
+#pragma unroll
+    for (int i = 0; i < XLD; ++i) {
+        const int src = s_src[(i * kThreads + tid) / kStepSeg];
+        xoff[i] = src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + (uint32_t)xseg * 16u : kOutOfRange;
+    }
+    uint4 xr[P][XLD];
+    auto issue_x = [&](int st, int s) {           // rows past `valid` and K past the end read 0
+        const bool in_k = s * 256 + xseg * 8 < K;
+#pragma unroll
+        for (int i = 0; i < XLD; ++i)
+            xr[st][i] = load16(ra, in_k && xoff[i] != kOutOfRange ? xoff[i] + (uint32_t)s * 512u
+                                                                  : kOutOfRange, 0);
+    };
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+        issue_x(s, s);
+
+    f32x4 acc[TPW][NMS];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+        for (int ms = 0; ms < NMS; ++ms)
             acc[tt][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
-    const f16x2 k64 = {(_Float16)64.0f, (_Float16)64.0f};
 
-    // group gi from stage s over NMS 16-row blocks, reading activations at
-    // 16-byte segment seg0 (+ lane offsets) of the LDS rows starting at abuf.
-    // A group past the last one (gi >= NG, in a padded trip) contributes
-    // exactly nothing: its scale is taken as 0 and every index is clamped.
-    auto group = [&](int s, const uint4 *abuf, int pitch, int seg0, int gi, auto nms_tag) {
-        constexpr int NMS = decltype(nms_tag)::value;
-        f16x2 c1024[TPW], c64[TPW];
-        float scale[TPW];
-        const int gc = min(gi, NG - 1);
+    // ---- 4. K loop, one line step per iteration: the step's activations
+    // into LDS (reordered per 8), one barrier (everyone is done with the step
+    // two back, whose buffer this one reuses), the step's groups, then the
+    // loads of the step P ahead. Steps past the end read zeros and their
+    // groups have scale 0.
+    for (int s0 = 0; s0 < NS; s0 += TRIP) {
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const uint32_t zb = lds_z[lds_row[tt] * NG + gc];
-            const f16x2 zz = as_h2(zb | (zb << 16));
-            c1024[tt] = zz + k1024;          // fp16(1024 + z), exact for |z| <= 1024
-            c64[tt] = zz + k64;
-            const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
-            scale[tt] = gi < NG ? sc : 0.0f;
-        }
-        f32x4 part[TPW][NMS];
+        for (int j = 0; j < TRIP; ++j) {
+            const int s = s0 + j;
+            const int st = j % P;
+            uint4 *xb = lds_x + (j & 1) * kBlockM * kStepPitch;
 #pragma unroll
-        for (int t = 0; t < kWords; ++t) {
-            f16x8 bop[TPW];
+            for (int i = 0; i < XLD; ++i)
+                xb[((i * kThreads + tid) / kStepSeg) * kStepPitch + xseg] = permute8(xr[st][i]);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            if (wave_live) {
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
-                bop[tt] = dequant8(frag_word<G>(bq[s][tt], t), c1024[tt], c64[tt]);
-            const int seg = seg0 + quarter * (G / 32) + t;   // this lane's 8 K positions
+                for (int h = 0; h < SG; ++h) {
+                    const int gi = s * SG + h;
+                    const int gc = min(gi, NG - 1);
+                    float scale[TPW];
+                    f16x2 c1024[TPW], c64[TPW];
 #pragma unroll
-            for (int ms = 0; ms < NMS; ++ms) {
-                const f16x8 aop = __builtin_bit_cast(f16x8, abuf[(ms * 16 + lrow) * pitch + seg]);
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt)
-                    part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        aop, bop[tt], t == 0 ? zero4 : part[tt][ms], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-            for (int ms = 0; ms < NMS; ++ms)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[tt][ms][i] += scale[tt] * part[tt][ms][i];
-    };
-
-    if constexpr (SINGLE) {
-        // the whole K of the tile's rows, once; every weight group of the wave
-        // is already in flight (D >= NG), so there is no loop at all
-        const int seg_row = K / 8;
-        const int n = kBlockM * seg_row;
-        for (int x0 = 0; x0 < n; x0 += 8 * kThreads) {
-            uint4 v[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int x = x0 + i * kThreads + tid;
-                const int r = min(x / seg_row, kBlockM - 1), sg = x - r * seg_row;
-                const int src = x < n ? s_src[r] : -1;
-                v[i] = load16(ra, src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + (uint32_t)sg * 16u
-                                           : kOutOfRange, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int x = x0 + i * kThreads + tid;
-                const int r = min(x / seg_row, kBlockM - 1), sg = x - r * seg_row;
-                if (x < n)
-                    lds_a[r * a_pitch + sg] = v[i];
-            }
-        }
-        __syncthreads();
-        auto run = [&](auto nms_tag) {
-            // all loads were issued before this point, so skipping the groups
-            // past NG cannot change the wait counts
-#pragma unroll
-            for (int gi = 0; gi < D; ++gi)
-                if (gi < NG)
-                    group(gi, lds_a, a_pitch, gi * (G / 8), gi, nms_tag);
-        };
-        if (valid > 16)
-            run(std::integral_constant<int, 2>{});
-        else
-            run(std::integral_constant<int, 1>{});
-    } else {
-        const int NC = (K + kChunkK - 1) / kChunkK;
-        static_assert(kThreads % kChunkSeg == 0, "a thread keeps one 16-byte column of a chunk");
-        constexpr int kRowStep = kThreads / kChunkSeg;
-        const int aseg = tid % kChunkSeg;         // this thread's 16-byte column of a chunk
-        const int arow0 = tid / kChunkSeg;        // and its rows arow0 + i * kRowStep
-        uint4 xr[kChunkLoads];
-        auto load_chunk = [&](int c) {            // rows past `valid` and K past the end read 0
-            const bool in_k = c * kChunkK + aseg * 8 < K;
-            const uint32_t col = (uint32_t)(c * kChunkK + aseg * 8) * 2u;
-#pragma unroll
-            for (int i = 0; i < kChunkLoads; ++i) {
-                const int src = s_src[arow0 + i * kRowStep];
-                xr[i] = load16(ra, in_k && src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + col
-                                                    : kOutOfRange, 0);
-            }
-        };
-        auto store_chunk = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < kChunkLoads; ++i)
-                lds_a[buf * kBlockM * kChunkPitch + (arow0 + i * kRowStep) * kChunkPitch + aseg] =
-                    GATED ? permute8(xr[i]) : xr[i];
-        };
-        load_chunk(0);
-        store_chunk(0);                           // read only after the loop's first barrier
-        // TRIP chunks per trip and no branch inside a trip (chunks past the
-        // end read activations as zero and their groups have scale 0), so the
-        // wait counts the compiler derives stay exact. Per chunk: load the
-        // next activation chunk into registers, one barrier (this chunk is in
-        // LDS, the other buffer is free), the chunk's groups each followed by
-        // the prefetch of the group kAhead chunks ahead, then store the next
-        // chunk.
-        auto run = [&](auto nms_tag) {
-            for (int c0 = 0; c0 < NC; c0 += TRIP) {
-#pragma unroll
-                for (int j = 0; j < TRIP; ++j) {
-                    const int c = c0 + j;
-                    load_chunk(c + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    __syncthreads();
-                    const uint4 *abuf = lds_a + (j & 1) * kBlockM * kChunkPitch;
-#pragma unroll
-                    for (int cs = 0; cs < CG; ++cs) {
-                        const int gi = c * CG + cs;
-                        group((j * CG + cs) % D, abuf, kChunkPitch, cs * (G / 8), gi, nms_tag);
-                        prefetch((j * CG + cs) % D, gi + D);
+                    for (int tt = 0; tt < TPW; ++tt) {
+                        zero_point_consts(lds_z[lds_row[tt] * NG + gc], c1024[tt], c64[tt]);
+                        const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
+                        scale[tt] = gi < NG ? sc : 0.0f;
                     }
-                    store_chunk((j & 1) ^ 1);
+                    f32x4 part[TPW][NMS];
+#pragma unroll
+                    for (int t = 0; t < kWords; ++t) {
+                        f16x8 bop[TPW];
+#pragma unroll
+                        for (int tt = 0; tt < TPW; ++tt)
+                            bop[tt] = dequant8(frag_word<G>(bq[st][tt][h], t), c1024[tt], c64[tt]);
+                        const int seg = h * (G / 8) + quarter * (G / 32) + t;   // this lane's 8 K positions
+#pragma unroll
+                        for (int ms = 0; ms < NMS; ++ms) {
+                            const f16x8 aop = __builtin_bit_cast(f16x8, xb[(ms * 16 + lrow) * kStepPitch + seg]);
+#pragma unroll
+                            for (int tt = 0; tt < TPW; ++tt)
+                                part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                    aop, bop[tt], t == 0 ? zero4 : part[tt][ms], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+                        for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                acc[tt][ms][i] += scale[tt] * part[tt][ms][i];
                 }
             }
-        };
-        if (valid > 16)
-            run(std::integral_constant<int, 2>{});
-        else
-            run(std::integral_constant<int, 1>{});
+            issue_x(st, s + P);
+            issue_w(st, s + P);
+        }
     }
 
+    // ---- 5. epilogue: H = gelu_tanh(gate) * up in fp16 at the tile's padded
+    // row, permuted per 8 columns. MFMA 16x16 output: lane holds rows
+    // 4 * quarter + i, column lrow.
     if (!wave_live)
         return;
-    // ---- epilogue. MFMA 16x16 output: lane holds rows 4*(lane/16)+i, column lane%16.
+    uint16_t *H = static_cast<uint16_t *>(p.out);
 #pragma unroll
-    for (int ms = 0; ms < 2; ++ms) {
+    for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = ms * 16 + quarter * 4 + i;
             if (r >= valid)
                 continue;
-            if constexpr (GATED) {
-                uint16_t *H = static_cast<uint16_t *>(p.out);
 #pragma unroll
-                for (int pp = 0; pp < TPW / 2; ++pp) {
-                    const int col = col_first + pp * 16 + lrow;
-                    const float h = gelu_tanh(acc[2 * pp][ms][i]) * acc[2 * pp + 1][ms][i];
-                    H[(size_t)(row0 + r) * p.n_out + permuted_col(col)] =
-                        __builtin_bit_cast(uint16_t, (_Float16)h);
-                }
-            } else {
-                const int f = p.sorted_ids[row0 + r];
-                float *Y = static_cast<float *>(p.out);
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt)
-                    Y[(size_t)f * p.n_out + col_first + tt * 16 + lrow] = acc[tt][ms][i];
+            for (int pp = 0; pp < TPW / 2; ++pp) {
+                const int col = col_first + pp * 16 + lrow;
+                const float h = gelu_tanh(acc[2 * pp][ms][i]) * acc[2 * pp + 1][ms][i];
+                H[(size_t)(row0 + r) * n_out + permuted_col(col)] =
+                    __builtin_bit_cast(uint16_t, (_Float16)h);
             }
         }
     }
 }
 
-// Shapes in use. gate_up streams K = d in chunks; down stages its whole
-// K = m once when m <= kSingleK and shares it among 8 waves whose register
-// budget (4 waves per SIMD) lets two workgroups share a CU.
-using GateUpShape = Shape<4, 4, 128, 2, 2>;
-using DownSingleShape = Shape<8, 2, 0, 0, 4>;
-using DownChunkShape = Shape<4, 2, 512, 2, 2>;
-
-template <int G, bool GATED, class S>
-size_t lds_bytes(int K)
+template <int G, class S>
+__global__ void __launch_bounds__(S::kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(S::kWpe))) gate_up_kernel(GemmArgs p)
 {
-    const bool single = S::kChunkK == 0;
-    const size_t pitch = single ? (size_t)K / 8 + 1 : (size_t)S::kChunkK / 8 + 1;
-    const size_t a = single ? kBlockM * pitch : 2 * kBlockM * pitch;
-    const size_t range_rows = (size_t)S::kWaves * S::kTiles * 8;
-    return sizeof(uint4) * a + 2 * sizeof(uint16_t) * 2 * range_rows * (size_t)(K / G);
+    // workgroup -> (N-block, tile), XCD-aware: consecutive workgroups go to
+    // the XCDs in turn, so XCD x takes tiles x, x + 8, ... and runs all
+    // N-blocks of a tile back to back, its activation rows staying in L2
+    constexpr int kColsPerWg = S::kWaves * S::kTiles / 2 * 16;
+    const int nblocks = (p.n_out + kColsPerWg - 1) / kColsPerWg;
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int nb = slot % nblocks;
+    const int tile = slot / nblocks * kXcds + xcd;
+    if (tile >= p.max_tiles)
+        return;
+    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    if (info.x < 0)
+        return;
+    if ((p.K + 255) / 256 == kGuSteps) {
+        if (info.y > 16)
+            gate_up_body<G, S, 2, kGuSteps>(p, info.x, info.y, tile * kBlockM, nb);
+        else
+            gate_up_body<G, S, 1, kGuSteps>(p, info.x, info.y, tile * kBlockM, nb);
+    } else {
+        if (info.y > 16)
+            gate_up_body<G, S, 2, 0>(p, info.x, info.y, tile * kBlockM, nb);
+        else
+            gate_up_body<G, S, 1, 0>(p, info.x, info.y, tile * kBlockM, nb);
+    }
 }
 
-template <int G, bool GATED, class S>
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
+template <int G, class S>
+size_t gate_up_lds_bytes(int K)
 {
-    constexpr int cols_per_wg = S::kWaves * (GATED ? S::kTiles / 2 : S::kTiles) * 16;
+    const size_t range_rows = (size_t)S::kWaves * S::kTiles / 2 * 16;
+    return sizeof(uint4) * 2 * kBlockM * kStepPitch + 2 * sizeof(uint16_t) * 2 * range_rows * (size_t)(K / G);
+}
+
+// ===========================================================================
+// down
+//   kWaves  waves per workgroup
+//   kAhead  weight row tiles (16 rows, all of K) in flight per wave
+//   kTiles  row tiles per wave (static: the loop is fully unrolled)
+//   kWpe    waves per SIMD the register budget is sized for
+template <int W, int P, int RT, int WPE>
+struct DnShape {
+    static constexpr int kWaves = W;
+    static constexpr int kAhead = P;
+    static constexpr int kTiles = RT;
+    static constexpr int kWpe = WPE;
+};
+using DownShape = DnShape<4, 2, 11, 2>;
+constexpr int kDnGroups = 11;       // K / 64 of the layer's down projection (m = 704)
+
+// NGC: groups per weight tile, known at compile time. Groups past K / G (a
+// generic instantiation rounded up) read no weights and have scale 0.
+template <int G, class S, int NMS, int NGC>
+__device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, int row0, int part)
+{
+    constexpr int WAVES = S::kWaves;
+    constexpr int P = S::kAhead;
+    constexpr int RT = S::kTiles;
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kWords = G / 32;
+    constexpr int kPartTiles = WAVES * RT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15;
+    const int quarter = lane >> 4;
+    const int K = p.K;
+    const int NG = K / G;
+    const int n_out = p.n_out;
+    const size_t wexp = (size_t)e * p.n_w;
+    // this part's row tiles: [rt0, rt0 + nrt) of the n_out / 16 weight tiles
+    const int rt0 = part * kPartTiles;
+    const int nrt = min(kPartTiles, n_out / 16 - rt0);
+    const int rows_part = nrt * 16;
+
+    extern __shared__ uint4 lds[];
+    const int a_pitch = K / 8 + 1;                                  // uint4 per activation row
+    uint4 *lds_a = lds;                                             // [32][a_pitch]
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + kBlockM * a_pitch);   // [part rows][NG]
+    uint16_t *lds_z = lds_s + kPartTiles * 16 * NG;
+    __shared__ int s_dst[kBlockM];
+
+    // ---- 1. scale/zero of the part's rows (one contiguous range each), row
+    // ids, the first weight tiles of this wave, then the activation rows
+    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    const int sz_seg = (rows_part * NG * 2 + 15) / 16;              // 16-byte segments per array
+    const uint32_t sz_base = (uint32_t)(rt0 * 16 * NG) * 2u;
+    constexpr int kSzLoads = 4;
+    uint4 sv[kSzLoads], zv[kSzLoads];
+#pragma unroll
+    for (int i = 0; i < kSzLoads; ++i) {
+        const int x = i * kThreads + tid;
+        const uint32_t off = x < sz_seg ? sz_base + (uint32_t)x * 16u : kOutOfRange;
+        sv[i] = load16(rs, off, 0);
+        zv[i] = load16(rz, off, 0);
+    }
+    int fid = 0;
+    if (tid < kBlockM)
+        fid = p.sorted_ids[row0 + tid];
+
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
+    // wave w takes row tiles rt0 + w, rt0 + w + WAVES, ...; tiles past the
+    // part read no weights and store nothing
+    auto tile_live = [&](int j) { return wave + j * WAVES < nrt; };
+    auto tile_row = [&](int j) { return (rt0 + wave + j * WAVES) * 16; };   // first weight row
+    Frag<G> bq[P][NGC];
+    auto issue_w = [&](int st, int j) {
+        const uint32_t voff = j < RT && tile_live(j)
+                                  ? (uint32_t)(tile_row(j) + lrow) * (uint32_t)(K / 2) +
+                                        (uint32_t)(quarter * (G / 8))
+                                  : kOutOfRange;
+#pragma unroll
+        for (int g = 0; g < NGC; ++g)
+            bq[st][g] = load_frag<G>(rq, g < NG ? voff : kOutOfRange, (uint32_t)(g * (G / 2)));
+    };
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        issue_w(j, j);
+
+    // activation rows row0 .. row0 + 16 NMS, already in the permuted K order
+    // (rows past `valid` read 0)
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
+    const int seg_row = K / 8;
+    const int a_total = 16 * NMS * seg_row;
+    for (int x0 = 0; x0 < a_total; x0 += 8 * kThreads) {
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int x = x0 + i * kThreads + tid;
+            const int r = min(x / seg_row, 16 * NMS - 1), sg = x - r * seg_row;
+            v[i] = load16(ra, x < a_total && r < valid
+                                  ? (uint32_t)(row0 + r) * (uint32_t)K * 2u + (uint32_t)sg * 16u
+                                  : kOutOfRange, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int x = x0 + i * kThreads + tid;
+            const int r = min(x / seg_row, 16 * NMS - 1), sg = x - r * seg_row;
+            if (x < a_total)
+                lds_a[r * a_pitch + sg] = v[i];
+        }
+    }
+    {
+        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
+        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
+#pragma unroll
+        for (int i = 0; i < kSzLoads; ++i) {
+            const int x = i * kThreads + tid;
+            if (x < sz_seg) {
+                ls[x] = sv[i];
+                lz[x] = zv[i];
+            }
+        }
+        for (int x = kSzLoads * kThreads + tid; x < sz_seg; x += kThreads) {   // large K only
+            ls[x] = load16(rs, sz_base + (uint32_t)x * 16u, 0);
+            lz[x] = load16(rz, sz_base + (uint32_t)x * 16u, 0);
+        }
+    }
+    if (tid < kBlockM)
+        s_dst[tid] = tid < valid ? fid : -1;
+    __syncthreads();
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // the MFMAs take the weights as the row operand: a lane ends with four
+    // consecutive output columns (weight rows 4 * quarter + i) of assignment
+    // row lrow (+16 for the second block)
+    int dst[NMS];
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+        dst[ms] = s_dst[ms * 16 + lrow];
+    f32x4 out[RT][NMS];
+
+    // ---- 2. stream this wave's row tiles, as straight-line code
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+        const int st = j % P;
+        // the activation reads are the same for every tile: an opaque offset
+        // keeps the compiler from holding all of them in registers
+        int aoff = 0;
+        asm volatile("" : "+v"(aoff));
+        const int srow = min(tile_row(j) - rt0 * 16, max(0, rows_part - 16));   // first row in lds_s/lds_z
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            out[j][ms] = zero4;
+#pragma unroll
+        for (int g = 0; g < NGC; ++g) {
+            const int gc = min(g, NG - 1);
+            f16x2 c1024, c64;
+            zero_point_consts(lds_z[(srow + lrow) * NG + gc], c1024, c64);
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float v = (float)__builtin_bit_cast(_Float16, lds_s[(srow + quarter * 4 + i) * NG + gc]);
+                sc[i] = g < NG ? v : 0.0f;
+            }
+            f32x4 prt[NMS];
+#pragma unroll
+            for (int t = 0; t < kWords; ++t) {
+                const f16x8 bop = dequant8(frag_word<G>(bq[st][g], t), c1024, c64);
+                const int seg = gc * (G / 8) + quarter * (G / 32) + t;
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+                    const f16x8 aop = __builtin_bit_cast(f16x8, lds_a[aoff + (ms * 16 + lrow) * a_pitch + seg]);
+                    prt[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop, aop, t == 0 ? zero4 : prt[ms], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[j][ms][i] += sc[i] * prt[ms][i];
+            // pin the accumulation here: otherwise the compiler sinks every
+            // tile's multiply-adds to the stores and keeps all partials live
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+                asm volatile("" : "+v"(out[j][ms]));
+        }
+        issue_w(st, j + P);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- 3. outputs: fp32 Y at each assignment's flat slot, one 16-byte
+    // store per assignment row and tile
+    float *Y = static_cast<float *>(p.out);
+#pragma unroll
+    for (int j = 0; j < RT; ++j) {
+        if (!tile_live(j))
+            continue;
+        const int col = tile_row(j) + quarter * 4;
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            if (dst[ms] >= 0)
+                *reinterpret_cast<f32x4 *>(Y + (size_t)dst[ms] * n_out + col) = out[j][ms];
+    }
+}
+
+template <int G, class S>
+__global__ void __launch_bounds__(S::kWaves * 64)
+__attribute__((amdgpu_waves_per_eu(S::kWpe))) down_kernel(GemmArgs p, int parts)
+{
+    // workgroup -> (part, tile), XCD-aware as in gate_up
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int part = slot % parts;
+    const int tile = slot / parts * kXcds + xcd;
+    if (tile >= p.max_tiles)
+        return;
+    const int2 info = p.tile_info[tile];
+    if (info.x < 0)
+        return;
+    const int ng = p.K / G;
+    // group counts with an instantiation: the layer's (11 groups of 64), else
+    // the next of 12 / 24 groups of 64 (6 / 12 of 128) with idle groups masked
+    constexpr int kSmall = 768 / G, kLarge = 1536 / G;
+    if (G == 64 && ng == kDnGroups) {
+        if (info.y > 16)
+            down_body<G, S, 2, kDnGroups>(p, info.x, info.y, tile * kBlockM, part);
+        else
+            down_body<G, S, 1, kDnGroups>(p, info.x, info.y, tile * kBlockM, part);
+    } else if (ng <= kSmall) {
+        if (info.y > 16)
+            down_body<G, S, 2, kSmall>(p, info.x, info.y, tile * kBlockM, part);
+        else
+            down_body<G, S, 1, kSmall>(p, info.x, info.y, tile * kBlockM, part);
+    } else {
+        if (info.y > 16)
+            down_body<G, S, 2, kLarge>(p, info.x, info.y, tile * kBlockM, part);
+        else
+            down_body<G, S, 1, kLarge>(p, info.x, info.y, tile * kBlockM, part);
+    }
+}
+
+template <int G, class S>
+size_t down_lds_bytes(int K)
+{
+    const size_t part_rows = (size_t)S::kWaves * S::kTiles * 16;
+    return sizeof(uint4) * kBlockM * ((size_t)K / 8 + 1) +
+           2 * sizeof(uint16_t) * part_rows * (size_t)(K / G);
+}
+
+template <class Kern>
+hipError_t allow_lds(Kern kern, size_t lds, size_t &allowed)
+{
+    if (lds <= allowed)
+        return hipSuccess;
+    const hipError_t err =
+        hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err == hipSuccess)
+        allowed = lds;
+    return err;
+}
+
+template <int G>
+hipError_t launch_gate_up_g(const GemmArgs &a, hipStream_t stream)
+{
+    using S = GateUpShape;
+    constexpr int cols_per_wg = S::kWaves * S::kTiles / 2 * 16;
     const int nblocks = (a.n_out + cols_per_wg - 1) / cols_per_wg;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    const size_t lds = lds_bytes<G, GATED, S>(a.K);
-    auto kern = moe_gemm_kernel<G, GATED, S>;
-    static size_t lds_allowed = 64 * 1024;   // raised once per instantiation when needed
-    if (lds > lds_allowed) {
-        hipError_t err = hipFuncSetAttribute((const void *)kern,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (err != hipSuccess)
-            return err;
-        lds_allowed = lds;
-    }
+    auto kern = gate_up_kernel<G, S>;
+    static size_t allowed = 64 * 1024;              // raised once per instantiation when needed
+    const size_t lds = gate_up_lds_bytes<G, S>(a.K);
+    hipError_t err = allow_lds(kern, lds, allowed);
+    if (err != hipSuccess)
+        return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
     kern<<<dim3(tiles * nblocks), dim3(S::kWaves * 64), lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_down_g(const GemmArgs &a, hipStream_t stream)
+{
+    using S = DownShape;
+    if (a.max_tiles == 0)
+        return hipSuccess;
+    const int parts = (a.n_out / 16 + S::kWaves * S::kTiles - 1) / (S::kWaves * S::kTiles);
+    auto kern = down_kernel<G, S>;
+    static size_t allowed = 64 * 1024;
+    const size_t lds = down_lds_bytes<G, S>(a.K);
+    hipError_t err = allow_lds(kern, lds, allowed);
+    if (err != hipSuccess)
+        return err;
+    const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
+    kern<<<dim3(tiles * parts), dim3(S::kWaves * 64), lds, stream>>>(a, parts);
     return hipGetLastError();
 }
 
@@ -551,27 +758,20 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream)
 size_t gemm_lds_bytes(bool gated, int K, int g)
 {
     if (gated)
-        return g == 128 ? lds_bytes<128, true, GateUpShape>(K) : lds_bytes<64, true, GateUpShape>(K);
-    if (K <= kSingleK)
-        return g == 128 ? lds_bytes<128, false, DownSingleShape>(K)
-                        : lds_bytes<64, false, DownSingleShape>(K);
-    return g == 128 ? lds_bytes<128, false, DownChunkShape>(K)
-                    : lds_bytes<64, false, DownChunkShape>(K);
+        return g == 128 ? gate_up_lds_bytes<128, GateUpShape>(K) : gate_up_lds_bytes<64, GateUpShape>(K);
+    return g == 128 ? down_lds_bytes<128, DownShape>(K) : down_lds_bytes<64, DownShape>(K);
 }
+
+int down_max_k() { return 1536; }
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
-    return g == 128 ? launch_gemm<128, true, GateUpShape>(a, stream)
-                    : launch_gemm<64, true, GateUpShape>(a, stream);
+    return g == 128 ? launch_gate_up_g<128>(a, stream) : launch_gate_up_g<64>(a, stream);
 }
 
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
 {
-    if (a.K <= kSingleK)
-        return g == 128 ? launch_gemm<128, false, DownSingleShape>(a, stream)
-                        : launch_gemm<64, false, DownSingleShape>(a, stream);
-    return g == 128 ? launch_gemm<128, false, DownChunkShape>(a, stream)
-                    : launch_gemm<64, false, DownChunkShape>(a, stream);
+    return g == 128 ? launch_down_g<128>(a, stream) : launch_down_g<64>(a, stream);
 }
 
 }  // namespace dgw4
