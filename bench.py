@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,6 +54,40 @@ def layer_bytes(shape, populated: int) -> dict:
         down=populated * dn_w + A * m * 2 + A * d * 4,               # H read + Y written (fp32)
         weights=populated * (gu_w + dn_w),
     )
+
+
+TRAFFIC_PROFILE = "profiles/moe_gemm_T256_hbm_traffic.md"
+TRAFFIC_SOURCES = ("w4a16_grouped_moe_amd/csrc/moe_gemm.hip",
+                   "w4a16_grouped_moe_amd/csrc/dgw4_internal.hpp")
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic() -> dict | None:
+    """HBM bytes per launch of the two GEMM kernels from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
+    for a plain copy of known size), or None when the GEMM sources changed
+    since the counters were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_PROFILE)
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_sha256") != gemm_source_hash():
+        return None
+    return rec
 
 
 def cpu_baseline(shape):
@@ -187,6 +222,7 @@ def main() -> int:
         f"{gbps:.1f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
     log(f"[bench] stages (us): {stage_us}; gate_up {gu_gbps:.1f} GB/s, down {dn_gbps:.1f} GB/s")
 
+    traffic = measured_traffic()
     pages_gbps = layers[0]["bytes"]["layer"] / (GB10_LAYER_MS * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -227,13 +263,14 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic["gate_up"]["bytes_per_launch"] if traffic else None,
             "bytes_per_launch": layers[0]["bytes"]["gate_up"],
             "us_per_launch": stage_us["gate_up"],
         },
         "down_kernel": {"achieved": round(dn_gbps, 1), "unit": "GB/s",
                         "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
-                        "bytes_per_launch": layers[0]["bytes"]["down"]},
+                        "bytes_per_launch": layers[0]["bytes"]["down"],
+                        "traffic": traffic["down"]["bytes_per_launch"] if traffic else None},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(CONFIGS["full"])
