@@ -51,7 +51,7 @@ def layer_bytes(shape, populated: int) -> dict:
     return dict(
         layer=populated * (gu_w + dn_w) + x + out + route,
         gate_up=populated * gu_w + x + A * m * 2,                    # + H written (fp16)
-        down=populated * dn_w + A * m * 2 + A * d * 4,               # H read + Y written (fp32)
+        down=populated * dn_w + A * m * 2 + A * d * 2,               # H read + Y written (fp16)
         weights=populated * (gu_w + dn_w),
     )
 
@@ -257,7 +257,7 @@ def main() -> int:
         "bytes_per_layer": layers[0]["bytes"]["layer"],
         "stage_us": stage_us,
         "roofline": {
-            "kernel": "gate_up_kernel<128> (gate_up + GELU(tanh) gate)",
+            "kernel": "gate_up4_kernel (gate_up + GELU(tanh) gate, layer shape)",
             "bound": "hbm",
             "achieved": round(gu_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -140,9 +140,9 @@ DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int blo
  *   out[t] = sum over k = 0..topk-1 (ascending) of
  *            w[t,k] * down_e( gelu_tanh(gate_e(x[t])) * up_e(x[t] ) ),  e = ids[t,k]
  * with expert weights dequantised as w = (q - z) * s. Accumulation is fp32;
- * the gated intermediate is rounded to fp16 once, each expert output is kept
- * in fp32 and the combine sums in ascending k in fp32 without atomics, then
- * rounds once to fp16. Repeated calls on the same inputs give bit-identical
+ * the gated intermediate and each expert output are rounded to fp16 once,
+ * and the combine sums w[t,k] * output in ascending k in fp32 without
+ * atomics, then rounds once to fp16. Repeated calls on the same inputs give bit-identical
  * results.
  *
  *   x          device fp16 bits [T, d]

@@ -34,8 +34,8 @@ def test_align_capacity():
 def test_workspace_query():
     n = dg.workspace_bytes(256, 8, 128, 2816, 704)
     cap = 256 * 8 + 128 * 31
-    # H fp16 [cap, m] + Y fp32 [A, d] + alignment buffers
-    data = cap * 704 * 2 + 2048 * 2816 * 4
+    # H fp16 [cap, m] + Y fp16 [A, d] + alignment buffers
+    data = cap * 704 * 2 + 2048 * 2816 * 2
     assert data <= n < data + 64 * 1024
     assert n % 256 == 0
 

@@ -7,10 +7,11 @@
 // (fixed-order reduction instead of index_add_).
 //
 // out[t, c] = fp16( sum_{k = 0..topk-1, ascending} w[t, k] * Y[t*topk + k, c] )
-// in fp32, skipping k whose expert id is outside [0, E). Each thread owns four
-// neighbouring columns of one token: 16-byte loads of Y, one 8-byte store.
-// Every output element is produced by exactly one thread with a fixed
-// sequence of operations, so the result is bitwise reproducible.
+// in fp32 (Y holds fp16 expert outputs), skipping k whose expert id is
+// outside [0, E). Each thread owns four neighbouring columns of one token:
+// 8-byte loads of Y, one 8-byte store. Every output element is produced by
+// exactly one thread with a fixed sequence of operations, so the result is
+// bitwise reproducible.
 #include "dgw4_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -18,7 +19,9 @@
 namespace dgw4 {
 namespace {
 
-__global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__ y,
+__device__ inline float h2f(uint32_t bits) { return (float)__builtin_bit_cast(_Float16, (uint16_t)bits); }
+
+__global__ void __launch_bounds__(256) combine_kernel(const uint2 *__restrict__ y,
                                                       const int32_t *__restrict__ ids,
                                                       const float *__restrict__ w, int topk,
                                                       int E, int d4, uint2 *__restrict__ out)
@@ -33,11 +36,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__
         if (e < 0 || e >= E)
             continue;
         const float wk = w[(size_t)t * topk + k];
-        const float4 v = y[((size_t)t * topk + k) * d4 + c4];
-        a0 = __fadd_rn(a0, __fmul_rn(wk, v.x));
-        a1 = __fadd_rn(a1, __fmul_rn(wk, v.y));
-        a2 = __fadd_rn(a2, __fmul_rn(wk, v.z));
-        a3 = __fadd_rn(a3, __fmul_rn(wk, v.w));
+        const uint2 v = y[((size_t)t * topk + k) * d4 + c4];
+        a0 = __fadd_rn(a0, __fmul_rn(wk, h2f(v.x & 0xFFFFu)));
+        a1 = __fadd_rn(a1, __fmul_rn(wk, h2f(v.x >> 16)));
+        a2 = __fadd_rn(a2, __fmul_rn(wk, h2f(v.y & 0xFFFFu)));
+        a3 = __fadd_rn(a3, __fmul_rn(wk, h2f(v.y >> 16)));
     }
     const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);   // RN-even
     const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
@@ -48,14 +51,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const float4 *__restrict__
 
 }  // namespace
 
-hipError_t launch_combine(const float *y, const int32_t *topk_ids, const float *topk_w,
+hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
                           int T, int topk, int E, int d, uint16_t *out, hipStream_t stream)
 {
     if (T == 0)
         return hipSuccess;
     const int d4 = d / 4;
     const dim3 grid((d4 + 255) / 256, T);
-    combine_kernel<<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const float4 *>(y), topk_ids,
+    combine_kernel<<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const uint2 *>(y), topk_ids,
                                                    topk_w, topk, E, d4,
                                                    reinterpret_cast<uint2 *>(out));
     return hipGetLastError();

@@ -32,7 +32,7 @@ int from_hip(hipError_t e)
 
 // Workspace of one forward call: alignment buffers, x in the GEMM's K order,
 // the gated intermediate H (fp16, one row per padded assignment) and the
-// per-assignment expert outputs Y (fp32, one row per flat assignment id).
+// per-assignment expert outputs Y (fp16, one row per flat assignment id).
 struct Layout {
     size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, total;
 };
@@ -53,7 +53,7 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
-    L.y = take(sizeof(float) * (size_t)A * (size_t)d);
+    L.y = take(sizeof(uint16_t) * (size_t)A * (size_t)d);
     L.total = off;
     return L;
 }
@@ -150,7 +150,8 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     if (cap == 0 || A > INT_MAX)
         return DGW4_ERR_INVALID_ARG;
     if (dgw4::gemm_lds_bytes(true, d, gu_g) > kMaxGemmLds ||
-        dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds || m > dgw4::down_max_k())
+        dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds || m > dgw4::down_max_k() ||
+        d / gu_g > dgw4::gate_up_max_groups())
         return DGW4_ERR_UNSUPPORTED;
     // the GEMMs address x, H and one expert's packed weights with 32-bit offsets
     if ((long long)T * d * 2 >= (1LL << 31) || (long long)cap * m * 2 >= (1LL << 31) ||
@@ -186,7 +187,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
-    float *y = reinterpret_cast<float *>(ws + L.y);
+    uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
 
     hipError_t err = mark(0);
     if (err == hipSuccess)

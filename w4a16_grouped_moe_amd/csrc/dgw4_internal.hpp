@@ -33,6 +33,9 @@ size_t gemm_lds_bytes(bool gated, int K, int g);
 // Largest contraction width (m) the down GEMM supports.
 int down_max_k();
 
+// Largest group count along K (d / g) the gate_up GEMM supports.
+int gate_up_max_groups();
+
 struct GemmArgs {
     const uint16_t *a_src;      // gate_up: x [T, d] (natural order); down: H [cap, m] (permuted per 8)
     int a_rows;                 // rows of a_src (T or cap)
@@ -47,13 +50,13 @@ struct GemmArgs {
     int topk;
     int A;                      // T * topk; also the pad sentinel in sorted_ids
     int max_tiles;              // cap / kBlockM
-    void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp32 [A, d]
+    void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp16 [A, d]
 };
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
 
-hipError_t launch_combine(const float *y, const int32_t *topk_ids, const float *topk_w,
+hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
                           int T, int topk, int E, int d, uint16_t *out, hipStream_t stream);
 
 }  // namespace dgw4

@@ -11,15 +11,15 @@
 //
 // gfx950 design
 // -------------
-// Both GEMMs stream the packed weights straight from the canonical layout.
-// A lane (row = lane % 16, quarter = lane / 16) loads g/8 bytes (16 for
-// g = 128, 8 for g = 64) of one weight row per group, so the four quarters
-// cover one whole group of 16 rows. Dequantisation builds exact fp16
-// integers in registers: for a 32-bit word of nibbles n0..n7,
-// (w & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + n0, 1024 + n4) and
-// (w & 0x00F000F0) | 0x54005400 is (64 + n1, 64 + n5); the same on w >> 8
-// gives n2/n6 and n3/n7, and one packed fp16 subtract of (1024 + z) or
-// (64 + z) leaves q - z exactly. The MFMA operand therefore holds K in the
+// Weights stream straight from the canonical layout. A lane (row = lane % 16,
+// quarter = lane / 16) loads g/8 bytes of one weight row per group, so the
+// four quarters cover one group of 16 rows; a wave reads whole 128-byte lines
+// of its rows (splitting a line between waves streams markedly slower).
+// Dequantisation builds exact fp16 integers in registers: for a word of
+// nibbles n0..n7, (w & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + n0,
+// 1024 + n4) and (w & 0x00F000F0) | 0x54005400 is (64 + n1, 64 + n5); the same
+// on w >> 8 gives n2/n6 and n3/n7, and one packed fp16 subtract of (1024 + z)
+// or (64 + z) leaves q - z exactly. The MFMA operand therefore holds K in the
 // order [0,4,1,5,2,6,3,7] per 8; the activations are used in the same order
 // (gate_up permutes x as it stages it, H is written permuted), which leaves
 // the contraction unchanged and needs no weight preshuffle.
@@ -27,33 +27,37 @@
 // the group's scale is applied once per output in fp32 (acc += s * partial),
 // so no weight is ever rounded by its scale.
 //
-// Loads complete in issue order, and the compiler's wait counting is exact
-// only in straight-line code without a vector store in flight: a loop back
-// edge, or a store issued while loads are pending, turns waits into waits for
-// the whole queue. So the step loops are fully unrolled for the layer's
-// shapes (K = 2816 and 704; other shapes take a generic loop), every wait is
-// for data issued a fixed number of steps earlier, and down keeps its outputs
-// in registers until its last tile.
+// Loads complete in issue order and the compiler's wait counting is exact only
+// in straight-line code, so every K loop is fully unrolled for the layer's
+// shapes and every wait is for data issued a fixed number of steps earlier.
+// Empty asm statements pin each group's accumulation in place (otherwise the
+// compiler sinks the multiply-adds to the epilogue and keeps every partial
+// live) and make LDS offsets opaque per step or group (otherwise later reads
+// are hoisted and held in registers).
 //
-// gate_up: workgroup = (32-row tile, 128 output columns), 8 waves, each wave
-// one 16-column gate tile and the matching up tile. K is walked in steps of
-// one 128-byte line of every weight row (256 K = two g=128 groups); the
-// weights and the activation slice of a step are loaded P = 2 steps ahead,
-// together, and the slice goes through a double-buffered LDS stage with one
-// barrier per step. Epilogue: gelu_tanh(gate) * up in fp32, H in fp16.
+// Activation rows re-read from L2 share each CU's vector-memory path with the
+// weight stream and measurably lower it, so the layer's shape (d = 2816,
+// m = 704, gate_up g = 128, down g = 64) takes wide-block kernels launched as
+// one 11-wave workgroup per CU (2 per 32-row tile, 256 for the 128 tiles of a
+// 256-token canvas):
+//   gate_up4: workgroup = (tile, 352 output columns); wave w owns pairs 2w and
+//     2w + 1 (16 gate columns and the matching up columns each) and computes
+//     them in two passes over K (11 line steps of 256 each), straight-line,
+//     with the loads of the second pass issued during the end of the first.
+//     The step's activation slice is staged in LDS once for the 11 waves.
+//   down4: workgroup = (tile, 1408 output columns = 88 weight row tiles); the
+//     tile's activations (all of K = 704) and the block's scales/zero points
+//     are staged in LDS once; wave w streams row tiles w, w + 11, ..., 2 tiles
+//     ahead, storing each tile's fp16 outputs as soon as it is done.
+// Other shapes take the generic kernels:
+//   gate_up_kernel: workgroup = (tile, 64 columns), 4 waves, one pair each.
+//   down_kernel: workgroup = (tile, 256 columns), 8 waves, two row tiles each,
+//     K in chunks of up to 768.
 //
-// down: workgroup = (32-row tile, part of 704 output columns), 4 waves. The
-// tile's activations (all of K) and the part's scales/zero points are staged
-// in LDS once; each wave then streams its 11 16-row weight tiles (all of K,
-// P = 2 tiles ahead) without any barrier. The MFMA takes the weights as its
-// row operand, so a lane ends with four consecutive output columns of one
-// assignment row: one 16-byte store of fp32 Y per row and tile, at the
-// assignment's flat slot t * topk + k.
-//
-// Both: tiles past the device-side total exit at once (static grid, no host
-// readback); the work items of one tile run back to back on one XCD so that
-// its activation rows stay in that XCD's L2; tiles with at most 16 valid rows
-// run one 16-row MFMA block instead of two.
+// All kernels: tiles past the device-side total exit at once (static grid, no
+// host readback); the workgroups of one tile run on one XCD so that its
+// activation rows stay in that XCD's L2; tiles with at most 16 valid rows run
+// one 16-row MFMA block instead of two.
 #include "dgw4_internal.hpp"
 
 namespace dgw4 {
@@ -165,6 +169,16 @@ __device__ inline uint4 permute8(uint4 v)
     return o;
 }
 
+// Four fp32 values rounded to fp16 (RN-even), packed in 8 bytes.
+__device__ inline uint2 pack_f16x4(f32x4 v)
+{
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)v[0]);
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)v[1]);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)v[2]);
+    const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)v[3]);
+    return make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+}
+
 // Position of column c inside its row when a row is stored permuted per 8
 // (the inverse of the K order [0,4,1,5,2,6,3,7]).
 __device__ inline int permuted_col(int c)
@@ -175,149 +189,123 @@ __device__ inline int permuted_col(int c)
 
 // ===========================================================================
 // gate_up
-//   kWaves  waves per workgroup
-//   kTiles  MFMA column tiles (16 weight rows each) per wave: gate and up
-//           alternate (tile 2p = gate rows, 2p + 1 = the matching up rows)
-//   kAhead  line steps (256 K) in flight per wave
-//   kWpe    waves per SIMD the register budget is sized for
-template <int W, int T, int P, int WPE>
-struct GuShape {
-    static constexpr int kWaves = W;
-    static constexpr int kTiles = T;
-    static constexpr int kAhead = P;
-    static constexpr int kWpe = WPE;
-};
-using GateUpShape = GuShape<8, 2, 2, 4>;
+//
+// Workgroup = (32-row tile, 64 output columns), 4 waves; wave w owns pair w
+// (16 gate columns and the matching 16 up columns) over all of K. K is
+// walked in line steps of 256 (one 128-byte line of every weight row: the
+// wave reads whole lines, which streams markedly faster than splitting a
+// line between waves). The step's activation slice is staged once in LDS for
+// the four waves. A workgroup needs 45 KB of LDS, so three fit on a CU.
+constexpr int kGuWaves = 4;
+constexpr int kGuThreads = kGuWaves * 64;
+constexpr int kGuCols = kGuWaves * 16;   // output columns per workgroup
+constexpr int kGuAhead = 3;         // weight line steps in flight per wave
 constexpr int kGuSteps = 11;        // line steps of K = 2816, the layer's hidden size
 constexpr int kStepSeg = 32;        // 16-byte activation segments per row and step
-constexpr int kStepPitch = kStepSeg + 1;   // +16 B per row: 16 rows at one segment hit 16 bank groups
+constexpr int kStepPitch = kStepSeg + 1;   // +16 B per row: 16 rows at one segment hit distinct banks
+constexpr int kGuMaxGroups = 64;    // K / G the scale/zero staging covers (4 loads per thread)
 
-// NSC > 0: the step count is a compile-time constant and the K loop is fully
-// unrolled; NSC = 0: a generic loop over ceil(K / 256) steps.
-template <int G, class S, int NMS, int NSC>
-__device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid, int row0, int nb)
+template <int G>
+constexpr size_t gate_up_lds_bytes_k(int K)
 {
-    constexpr int WAVES = S::kWaves;
-    constexpr int TPW = S::kTiles;
-    constexpr int P = S::kAhead;
-    constexpr int kThreads = WAVES * 64;
+    return sizeof(uint4) * 2 * kBlockM * kStepPitch +                  // activation stages
+           2 * sizeof(uint16_t) * 2 * kGuCols * (size_t)(K / G);        // scale, zero of 2 x 64 rows
+}
+
+// NSC > 0: K = 256 NSC exactly, a compile-time constant, and the K loop is
+// fully unrolled; NSC = 0: a generic loop over ceil(K / 256) steps.
+template <int G, int NMS, int NSC>
+__device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid, int row0, int cb,
+                                             const int (&fidr)[4])
+{
+    constexpr int P = kGuAhead;                   // weights P steps ahead
+    constexpr int PX = P - 1;                     // activations P - 1 steps ahead (L2 hits)
     constexpr int SG = 256 / G;                   // groups per line step
-    constexpr int kWords = G / 32;
-    constexpr int kColsPerWave = TPW / 2 * 16;
-    constexpr int kColsPerWg = WAVES * kColsPerWave;
-    constexpr int kRangeRows = kColsPerWg;        // gate rows (and up rows) of the workgroup
+    constexpr int kWords = G / 32;                // nibble words per lane and group
     constexpr int kRows = NMS * 16;               // activation rows staged
-    constexpr int XLD = kRows * kStepSeg / kThreads;
-    static_assert(kRows * kStepSeg % kThreads == 0 && kThreads % kStepSeg == 0, "activation split");
-    static_assert(TPW % 2 == 0, "gate/up tiles come in pairs");
-    constexpr int TRIP = NSC > 0 ? NSC : (P % 2 == 0 ? P : 2 * P);
+    constexpr int XLD = kRows * kStepSeg / kGuThreads;
+    static_assert(kRows * kStepSeg % kGuThreads == 0 && kGuThreads % kStepSeg == 0, "activation split");
+    constexpr int TRIP = NSC > 0 ? NSC : 2 * P * PX;   // multiple of P, PX and 2 (LDS stage parity)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
     const int lrow = lane & 15;
     const int quarter = lane >> 4;
-    const int K = p.K;
+    const int K = NSC > 0 ? NSC * 256 : p.K;
     const int NG = K / G;
     const int NS = NSC > 0 ? NSC : (K + 255) / 256;
     const int n_out = p.n_out;
     const size_t wexp = (size_t)e * p.n_w;
-    // a wave past the last column (n_out is a multiple of 16) loads no
+    const int col0 = cb * kGuCols;                // first gate column of the workgroup
+    const int pcol = col0 + wave * 16;            // first column of this wave's pair
+    // a pair past the last column (n_out is a multiple of 16) loads no
     // weights, skips the math and stores nothing; it still stages activations
-    const int col_first = nb * kColsPerWg + wave * kColsPerWave;
-    const bool wave_live = col_first < n_out;
-    const int range0 = nb * kColsPerWg;           // gate rows; up rows start at n_out + range0
+    const bool live = pcol < n_out;
 
     extern __shared__ uint4 lds[];
     uint4 *lds_x = lds;                                             // [2][32][kStepPitch]
-    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kBlockM * kStepPitch);   // [2 kRangeRows][NG]
-    uint16_t *lds_z = lds_s + 2 * kRangeRows * NG;
-    __shared__ int s_src[kBlockM];
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kBlockM * kStepPitch);   // [2 x 64 rows][NG]
+    uint16_t *lds_z = lds_s + 2 * kGuCols * NG;
 
-    // ---- 1. scale/zero loads (two contiguous row ranges), row ids, and the
-    // weights of the first P steps. Scale/zero are issued first, so waiting
-    // for them does not wait for weights.
-    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    constexpr int kSzLoads = 2;
-    const int range_seg = kRangeRows * NG / 8;     // 16-byte segments per range
+    // ---- 1. scale/zero loads (gate rows col0.., up rows n_out + col0..),
+    // then the activations and weights of the first steps. Loads complete in
+    // issue order: the row ids (issued at kernel entry) come first, then
+    // scale/zero, then per step the activations before the weights, so that
+    // waiting for a step's activations never waits for later weights.
+    const uint32_t sz_bytes = (uint32_t)p.n_w * (uint32_t)NG * 2u;
+    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, sz_bytes);
+    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, sz_bytes);
+    constexpr int kSzLoads = 4;                   // covers NG <= kGuMaxGroups
+    const int range_seg = kGuCols * NG / 8;       // 16-byte segments per 64-row range
     const int sz_total = 2 * range_seg;
     auto sz_off = [&](int x) -> uint32_t {
         if (x >= sz_total)
             return kOutOfRange;
         const int r = x >= range_seg;
-        return (uint32_t)(((r ? n_out : 0) + range0) * NG) * 2u + (uint32_t)(x - r * range_seg) * 16u;
+        return (uint32_t)(((r ? n_out : 0) + col0) * NG) * 2u + (uint32_t)(x - r * range_seg) * 16u;
     };
     uint4 sv[kSzLoads], zv[kSzLoads];
 #pragma unroll
     for (int i = 0; i < kSzLoads; ++i) {
-        const uint32_t off = sz_off(i * kThreads + tid);
+        const uint32_t off = sz_off(i * kGuThreads + tid);
         sv[i] = load16(rs, off, 0);
         zv[i] = load16(rz, off, 0);
     }
-    int fid = 0;
-    if (tid < kBlockM)
-        fid = p.sorted_ids[row0 + tid];           // row0 + tid < cap: always in the buffer
 
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2),
-                                wave_live ? (uint32_t)p.n_w * (uint32_t)(K / 2) : 0u);
-    uint32_t wvoff[TPW];
-    int lds_row[TPW];                              // this lane's row in the scale/zero ranges
+                                live ? (uint32_t)p.n_w * (uint32_t)(K / 2) : 0u);
+    // tile 0 = gate rows pcol + lrow, tile 1 = up rows n_out + pcol + lrow
+    uint32_t wvoff[2];
+    int lds_row[2];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int in_range = wave * kColsPerWave + (tt >> 1) * 16 + lrow;
-        const int wr = ((tt & 1) ? n_out : 0) + range0 + in_range;
-        lds_row[tt] = (tt & 1) * kRangeRows + in_range;
-        wvoff[tt] = (uint32_t)wr * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8));
+    for (int tt = 0; tt < 2; ++tt) {
+        lds_row[tt] = tt * kGuCols + wave * 16 + lrow;
+        wvoff[tt] = (uint32_t)((tt ? n_out : 0) + pcol + lrow) * (uint32_t)(K / 2) +
+                    (uint32_t)(quarter * (G / 8));
     }
-    Frag<G> bq[P][TPW][SG];
+    Frag<G> bq[P][2][SG];
     auto issue_w = [&](int st, int s) {           // step s into register stage st
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
+        for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int h = 0; h < SG; ++h) {
                 const int gi = s * SG + h;
                 bq[st][tt][h] = load_frag<G>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
-                                             (uint32_t)(s * 128 + h * (G / 2)));
+                                             (uint32_t)(gi * (G / 2)));
             }
     };
-#pragma unroll
-    for (int s = 0; s < P; ++s)
-        issue_w(s, s);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- 2. scale/zero and row sources into LDS
-    {
-        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
-        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
-#pragma unroll
-        for (int i = 0; i < kSzLoads; ++i) {
-            const int x = i * kThreads + tid;
-            if (x < sz_total) {
-                ls[x] = sv[i];
-                lz[x] = zv[i];
-            }
-        }
-        for (int x = kSzLoads * kThreads + tid; x < sz_total; x += kThreads) {   // large K only
-            ls[x] = load16(rs, sz_off(x), 0);
-            lz[x] = load16(rz, sz_off(x), 0);
-        }
-    }
-    if (tid < kBlockM)
-        s_src[tid] = tid < valid ? fid / p.topk : -1;
-    __syncthreads();
-
-    // ---- 3. activation slices: thread -> (row, 16-byte segment) of a step,
-    // the segment the same in every row it loads; the first P steps now
+    // activation slices: thread -> (rows tid / 32 + 8 i, 16-byte segment
+    // tid % 32) of a step; the row's source token comes from its assignment
+    // id (a pad entry, id >= A, reads zeros)
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
     const int xseg = tid % kStepSeg;
     uint32_t xoff[XLD];
 #pragma unroll
-    for (int i = 0; i < XLD; ++i) {
-        const int src = s_src[(i * kThreads + tid) / kStepSeg];
-        xoff[i] = src >= 0 ? (uint32_t)src * (uint32_t)K * 2u + (uint32_t)xseg * 16u : kOutOfRange;
-    }
-    uint4 xr[P][XLD];
+    for (int i = 0; i < XLD; ++i)
+        xoff[i] = fidr[i] < p.A ? (uint32_t)(fidr[i] / p.topk) * (uint32_t)K * 2u + (uint32_t)xseg * 16u
+                                : kOutOfRange;
+    uint4 xr[PX][XLD];
     auto issue_x = [&](int st, int s) {           // rows past `valid` and K past the end read 0
         const bool in_k = s * 256 + xseg * 8 < K;
 #pragma unroll
@@ -325,23 +313,43 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
             xr[st][i] = load16(ra, in_k && xoff[i] != kOutOfRange ? xoff[i] + (uint32_t)s * 512u
                                                                   : kOutOfRange, 0);
     };
+    issue_x(0, 0);
+    issue_w(0, 0);
 #pragma unroll
-    for (int s = 0; s < P; ++s)
-        issue_x(s, s);
+    for (int s = 1; s < P; ++s) {
+        if (s < PX)
+            issue_x(s, s);
+        issue_w(s, s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    f32x4 acc[TPW][NMS];
+    // ---- 2. scale/zero into LDS (made visible by the first step's barrier)
+    {
+        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
+        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
+        for (int i = 0; i < kSzLoads; ++i) {
+            const int x = i * kGuThreads + tid;
+            if (x < sz_total) {
+                ls[x] = sv[i];
+                lz[x] = zv[i];
+            }
+        }
+    }
+
+    f32x4 acc[2][NMS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms)
             acc[tt][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // ---- 4. K loop, one line step per iteration: the step's activations
+    // ---- 3. K loop, one line step per iteration: the step's activations
     // into LDS (reordered per 8), one barrier (everyone is done with the step
     // two back, whose buffer this one reuses), the step's groups, then the
-    // loads of the step P ahead. Steps past the end read zeros and their
-    // groups have scale 0.
+    // activations PX steps ahead and the weights P steps ahead. Steps past
+    // the end read zeros and their groups have scale 0.
     for (int s0 = 0; s0 < NS; s0 += TRIP) {
 #pragma unroll
         for (int j = 0; j < TRIP; ++j) {
@@ -350,41 +358,41 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
             uint4 *xb = lds_x + (j & 1) * kBlockM * kStepPitch;
 #pragma unroll
             for (int i = 0; i < XLD; ++i)
-                xb[((i * kThreads + tid) / kStepSeg) * kStepPitch + xseg] = permute8(xr[st][i]);
+                xb[((i * kGuThreads + tid) / kStepSeg) * kStepPitch + xseg] = permute8(xr[j % PX][i]);
             __builtin_amdgcn_sched_barrier(0);
             __syncthreads();
-            if (wave_live) {
+            if (live) {
 #pragma unroll
                 for (int h = 0; h < SG; ++h) {
                     const int gi = s * SG + h;
                     const int gc = min(gi, NG - 1);
-                    float scale[TPW];
-                    f16x2 c1024[TPW], c64[TPW];
+                    float scale[2];
+                    f16x2 c1024[2], c64[2];
 #pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt) {
+                    for (int tt = 0; tt < 2; ++tt) {
                         zero_point_consts(lds_z[lds_row[tt] * NG + gc], c1024[tt], c64[tt]);
                         const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
                         scale[tt] = gi < NG ? sc : 0.0f;
                     }
-                    f32x4 part[TPW][NMS];
+                    f32x4 part[2][NMS];
 #pragma unroll
                     for (int t = 0; t < kWords; ++t) {
-                        f16x8 bop[TPW];
+                        f16x8 bop[2];
 #pragma unroll
-                        for (int tt = 0; tt < TPW; ++tt)
+                        for (int tt = 0; tt < 2; ++tt)
                             bop[tt] = dequant8(frag_word<G>(bq[st][tt][h], t), c1024[tt], c64[tt]);
                         const int seg = h * (G / 8) + quarter * (G / 32) + t;   // this lane's 8 K positions
 #pragma unroll
                         for (int ms = 0; ms < NMS; ++ms) {
                             const f16x8 aop = __builtin_bit_cast(f16x8, xb[(ms * 16 + lrow) * kStepPitch + seg]);
 #pragma unroll
-                            for (int tt = 0; tt < TPW; ++tt)
+                            for (int tt = 0; tt < 2; ++tt)
                                 part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                     aop, bop[tt], t == 0 ? zero4 : part[tt][ms], 0, 0, 0);
                         }
                     }
 #pragma unroll
-                    for (int tt = 0; tt < TPW; ++tt)
+                    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                         for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
@@ -392,17 +400,18 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
                                 acc[tt][ms][i] += scale[tt] * part[tt][ms][i];
                 }
             }
-            issue_x(st, s + P);
+            issue_x(j % PX, s + PX);
             issue_w(st, s + P);
         }
     }
 
-    // ---- 5. epilogue: H = gelu_tanh(gate) * up in fp16 at the tile's padded
+    // ---- 4. epilogue: H = gelu_tanh(gate) * up in fp16 at the tile's padded
     // row, permuted per 8 columns. MFMA 16x16 output: lane holds rows
     // 4 * quarter + i, column lrow.
-    if (!wave_live)
+    if (!live)
         return;
     uint16_t *H = static_cast<uint16_t *>(p.out);
+    const int col = pcol + lrow;
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
@@ -410,181 +419,213 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
             const int r = ms * 16 + quarter * 4 + i;
             if (r >= valid)
                 continue;
-#pragma unroll
-            for (int pp = 0; pp < TPW / 2; ++pp) {
-                const int col = col_first + pp * 16 + lrow;
-                const float h = gelu_tanh(acc[2 * pp][ms][i]) * acc[2 * pp + 1][ms][i];
-                H[(size_t)(row0 + r) * n_out + permuted_col(col)] =
-                    __builtin_bit_cast(uint16_t, (_Float16)h);
-            }
+            const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
+            H[(size_t)(row0 + r) * n_out + permuted_col(col)] = __builtin_bit_cast(uint16_t, (_Float16)h);
         }
     }
 }
 
-template <int G, class S>
-__global__ void __launch_bounds__(S::kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(S::kWpe))) gate_up_kernel(GemmArgs p)
+template <int G>
+__global__ void __launch_bounds__(kGuThreads)
+__attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
 {
-    // workgroup -> (N-block, tile), XCD-aware: consecutive workgroups go to
-    // the XCDs in turn, so XCD x takes tiles x, x + 8, ... and runs all
-    // N-blocks of a tile back to back, its activation rows staying in L2
-    constexpr int kColsPerWg = S::kWaves * S::kTiles / 2 * 16;
-    const int nblocks = (p.n_out + kColsPerWg - 1) / kColsPerWg;
+    // workgroup -> (column block, tile), XCD-aware: consecutive workgroups go
+    // to the XCDs in turn, so XCD x takes tiles x, x + 8, ... and runs all
+    // column blocks of a tile back to back, its activation rows staying in L2
+    const int nblocks = (p.n_out + kGuCols - 1) / kGuCols;
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    const int nb = slot % nblocks;
+    const int cb = slot % nblocks;
     const int tile = slot / nblocks * kXcds + xcd;
     if (tile >= p.max_tiles)
         return;
+    // the assignment ids of the thread's activation rows (rows tid / 32 and
+    // tid / 32 + 8 of each 16-row block) go out together with the tile
+    // descriptor, so the activation loads need no further round trip
+    const int r0 = (int)threadIdx.x / kStepSeg;
+    int fidr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)                   // < cap: always in the buffer
+        fidr[i] = p.sorted_ids[tile * kBlockM + r0 + i * (kGuThreads / kStepSeg)];
     const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
     if (info.x < 0)
         return;
-    if ((p.K + 255) / 256 == kGuSteps) {
+    if (p.K == kGuSteps * 256) {
         if (info.y > 16)
-            gate_up_body<G, S, 2, kGuSteps>(p, info.x, info.y, tile * kBlockM, nb);
+            gate_up_body<G, 2, kGuSteps>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, S, 1, kGuSteps>(p, info.x, info.y, tile * kBlockM, nb);
+            gate_up_body<G, 1, kGuSteps>(p, info.x, info.y, tile * kBlockM, cb, fidr);
     } else {
         if (info.y > 16)
-            gate_up_body<G, S, 2, 0>(p, info.x, info.y, tile * kBlockM, nb);
+            gate_up_body<G, 2, 0>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, S, 1, 0>(p, info.x, info.y, tile * kBlockM, nb);
+            gate_up_body<G, 1, 0>(p, info.x, info.y, tile * kBlockM, cb, fidr);
     }
-}
-
-template <int G, class S>
-size_t gate_up_lds_bytes(int K)
-{
-    const size_t range_rows = (size_t)S::kWaves * S::kTiles / 2 * 16;
-    return sizeof(uint4) * 2 * kBlockM * kStepPitch + 2 * sizeof(uint16_t) * 2 * range_rows * (size_t)(K / G);
 }
 
 // ===========================================================================
 // down
-//   kWaves  waves per workgroup
-//   kAhead  weight row tiles (16 rows, all of K) in flight per wave
-//   kTiles  row tiles per wave (static: the loop is fully unrolled)
-//   kWpe    waves per SIMD the register budget is sized for
-template <int W, int P, int RT, int WPE>
-struct DnShape {
-    static constexpr int kWaves = W;
-    static constexpr int kAhead = P;
-    static constexpr int kTiles = RT;
-    static constexpr int kWpe = WPE;
-};
-using DownShape = DnShape<4, 2, 11, 2>;
+//
+// Workgroup = (32-row tile, 256 output columns = 16 weight row tiles), 8
+// waves; wave w owns row tiles w and w + 8 of the block. The tile's
+// activations (all of K, already in the permuted K order) and the block's
+// scales/zero points (transposed to [group][row]) are staged in LDS once;
+// each wave then streams its two weight tiles, K in chunks of CH groups,
+// with both tiles' loads in flight from the start. The MFMA takes the
+// weights as its row operand, so a lane ends with four consecutive output
+// columns of one assignment row: one 16-byte fp32 store per row and tile, at
+// the assignment's flat slot t * topk + k, issued after the last chunk.
+constexpr int kDnWaves = 8;
+constexpr int kDnThreads = kDnWaves * 64;
+constexpr int kDnTilesPerWave = 2;
+constexpr int kDnRows = kDnWaves * kDnTilesPerWave * 16;   // weight rows (output columns) per block
+constexpr int kDnAhead = 2;         // (tile, chunk) units in flight per wave
 constexpr int kDnGroups = 11;       // K / 64 of the layer's down projection (m = 704)
+constexpr int kALoads = 6;          // activation segments per thread and batch
 
-// NGC: groups per weight tile, known at compile time. Groups past K / G (a
-// generic instantiation rounded up) read no weights and have scale 0.
-template <int G, class S, int NMS, int NGC>
-__device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, int row0, int part)
+template <int G>
+size_t down_lds_bytes_k(int K)
 {
-    constexpr int WAVES = S::kWaves;
-    constexpr int P = S::kAhead;
-    constexpr int RT = S::kTiles;
-    constexpr int kThreads = WAVES * 64;
+    return sizeof(uint4) * kBlockM * ((size_t)K / 8 + 1) +
+           2 * sizeof(uint16_t) * kDnRows * (size_t)(K / G);
+}
+
+// Byte offset of 16-byte activation segment x of the tile's 32 rows (all of
+// K), or an out-of-range offset past them.
+__device__ inline uint32_t down_a_off(const GemmArgs &p, int row0, int x)
+{
+    const int seg_row = p.K / 8;
+    const int r = x / seg_row, sg = x - r * seg_row;
+    return x < kBlockM * seg_row ? (uint32_t)(row0 + r) * (uint32_t)p.K * 2u + (uint32_t)sg * 16u
+                                 : kOutOfRange;
+}
+
+// CH: groups per K chunk; NCH: chunks per weight tile (both compile-time).
+// EXACT: K = CH * NCH * G exactly (a compile-time constant); otherwise groups
+// past K / G (a rounded-up chunk) read no weights and have scale 0.
+template <int G, int NMS, int CH, int NCH, bool EXACT>
+__device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, int row0, int cb,
+                                          const uint4 (&av)[kALoads], int fid)
+{
+    constexpr int P = kDnAhead;
+    constexpr int NU = kDnTilesPerWave * NCH;   // units (tile j, chunk c), j-major
     constexpr int kWords = G / 32;
-    constexpr int kPartTiles = WAVES * RT;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15;
     const int quarter = lane >> 4;
-    const int K = p.K;
+    const int K = EXACT ? CH * NCH * G : p.K;
     const int NG = K / G;
     const int n_out = p.n_out;
     const size_t wexp = (size_t)e * p.n_w;
-    // this part's row tiles: [rt0, rt0 + nrt) of the n_out / 16 weight tiles
-    const int rt0 = part * kPartTiles;
-    const int nrt = min(kPartTiles, n_out / 16 - rt0);
-    const int rows_part = nrt * 16;
+    const int rt0 = cb * (kDnRows / 16);          // first weight row tile of the block
+    const int nrt = min(kDnRows / 16, n_out / 16 - rt0);
+    const int a_pitch = K / 8 + 1;                // uint4 per activation row
 
     extern __shared__ uint4 lds[];
-    const int a_pitch = K / 8 + 1;                                  // uint4 per activation row
     uint4 *lds_a = lds;                                             // [32][a_pitch]
-    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + kBlockM * a_pitch);   // [part rows][NG]
-    uint16_t *lds_z = lds_s + kPartTiles * 16 * NG;
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + kBlockM * a_pitch);   // [NG][kDnRows]
+    uint16_t *lds_z = lds_s + kDnRows * NG;
     __shared__ int s_dst[kBlockM];
 
-    // ---- 1. scale/zero of the part's rows (one contiguous range each), row
-    // ids, the first weight tiles of this wave, then the activation rows
+    // ---- 1. scale/zero of the block's rows (one contiguous range each),
+    // then the first weight units of this wave. The activation rows and row
+    // ids were issued at kernel entry, so they land first.
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    const int sz_seg = (rows_part * NG * 2 + 15) / 16;              // 16-byte segments per array
+    const int sz_seg = (nrt * 16 * NG * 2 + 15) / 16;             // 16-byte segments per array
     const uint32_t sz_base = (uint32_t)(rt0 * 16 * NG) * 2u;
-    constexpr int kSzLoads = 4;
+    constexpr int kSzLoads = 2;                   // 256 rows x NG <= 24 groups
+    static_assert(kDnRows * NCH * CH * 2 <= kSzLoads * kDnThreads * 16, "scale/zero loads");
     uint4 sv[kSzLoads], zv[kSzLoads];
 #pragma unroll
     for (int i = 0; i < kSzLoads; ++i) {
-        const int x = i * kThreads + tid;
+        const int x = i * kDnThreads + tid;
         const uint32_t off = x < sz_seg ? sz_base + (uint32_t)x * 16u : kOutOfRange;
         sv[i] = load16(rs, off, 0);
         zv[i] = load16(rz, off, 0);
     }
-    int fid = 0;
-    if (tid < kBlockM)
-        fid = p.sorted_ids[row0 + tid];
+    // activation rows row0 .. row0 + 16 NMS (staged whatever their content: a
+    // row past `valid` only feeds output rows that are never stored)
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
+    const int seg_row = K / 8;
+    const int a_total = 16 * NMS * seg_row;
+    auto a_put = [&](int x, uint4 v) {
+        const int r = min(x / seg_row, 16 * NMS - 1), sg = x - r * seg_row;
+        if (x < a_total)
+            lds_a[r * a_pitch + sg] = v;
+    };
 
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
-    // wave w takes row tiles rt0 + w, rt0 + w + WAVES, ...; tiles past the
-    // part read no weights and store nothing
-    auto tile_live = [&](int j) { return wave + j * WAVES < nrt; };
-    auto tile_row = [&](int j) { return (rt0 + wave + j * WAVES) * 16; };   // first weight row
-    Frag<G> bq[P][NGC];
-    auto issue_w = [&](int st, int j) {
-        const uint32_t voff = j < RT && tile_live(j)
+    auto tile_live = [&](int j) { return wave + j * kDnWaves < nrt; };
+    auto tile_row = [&](int j) { return (rt0 + wave + j * kDnWaves) * 16; };   // first weight row
+    Frag<G> bq[P][CH];
+    auto issue_w = [&](int st, int u) {
+        const int j = u / NCH, c = u % NCH;
+        const uint32_t voff = u < NU && tile_live(j)
                                   ? (uint32_t)(tile_row(j) + lrow) * (uint32_t)(K / 2) +
                                         (uint32_t)(quarter * (G / 8))
                                   : kOutOfRange;
 #pragma unroll
-        for (int g = 0; g < NGC; ++g)
-            bq[st][g] = load_frag<G>(rq, g < NG ? voff : kOutOfRange, (uint32_t)(g * (G / 2)));
-    };
-#pragma unroll
-    for (int j = 0; j < P; ++j)
-        issue_w(j, j);
-
-    // activation rows row0 .. row0 + 16 NMS, already in the permuted K order
-    // (rows past `valid` read 0)
-    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
-    const int seg_row = K / 8;
-    const int a_total = 16 * NMS * seg_row;
-    for (int x0 = 0; x0 < a_total; x0 += 8 * kThreads) {
-        uint4 v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int x = x0 + i * kThreads + tid;
-            const int r = min(x / seg_row, 16 * NMS - 1), sg = x - r * seg_row;
-            v[i] = load16(ra, x < a_total && r < valid
-                                  ? (uint32_t)(row0 + r) * (uint32_t)K * 2u + (uint32_t)sg * 16u
-                                  : kOutOfRange, 0);
+        for (int g = 0; g < CH; ++g) {
+            const int gi = c * CH + g;
+            bq[st][g] = load_frag<G>(rq, gi < NG ? voff : kOutOfRange, (uint32_t)(gi * (G / 2)));
         }
+    };
+
+    // ---- 2. activations, scale/zero (transposed) and row destinations into
+    // LDS. With one chunk (K <= 768) the activations fit one batch and the
+    // weights are issued right behind them; a longer K stages its
+    // activations in several batches first (the choice is compile-time, so
+    // every wait below counts only the loads it needs).
+    static_assert(NCH > 1 || 16 * 2 * (CH * G) / 8 <= kALoads * kDnThreads, "one activation batch");
+    uint4 avb[kALoads];
+    if constexpr (NCH == 1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int x = x0 + i * kThreads + tid;
-            const int r = min(x / seg_row, 16 * NMS - 1), sg = x - r * seg_row;
-            if (x < a_total)
-                lds_a[r * a_pitch + sg] = v[i];
+        for (int u = 0; u < P; ++u)
+            issue_w(u, u);
+    }
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i)
+        a_put(i * kDnThreads + tid, av[i]);
+    if constexpr (NCH > 1) {
+        for (int x0 = kALoads * kDnThreads; x0 < a_total; x0 += kALoads * kDnThreads) {
+#pragma unroll
+            for (int i = 0; i < kALoads; ++i)
+                avb[i] = load16(ra, down_a_off(p, row0, x0 + i * kDnThreads + tid), 0);
+#pragma unroll
+            for (int i = 0; i < kALoads; ++i)
+                a_put(x0 + i * kDnThreads + tid, avb[i]);
         }
     }
     {
-        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
-        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
+        // element x of the block's [rows][NG] range -> lds [g][row]
+        auto put8 = [&](uint16_t *dst, int x, uint4 v) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int el = x * 8 + k;
+                const int r = el / NG, g = el - r * NG;
+                if (r < nrt * 16)
+                    dst[g * kDnRows + r] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+            }
+        };
 #pragma unroll
         for (int i = 0; i < kSzLoads; ++i) {
-            const int x = i * kThreads + tid;
+            const int x = i * kDnThreads + tid;
             if (x < sz_seg) {
-                ls[x] = sv[i];
-                lz[x] = zv[i];
+                put8(lds_s, x, sv[i]);
+                put8(lds_z, x, zv[i]);
             }
-        }
-        for (int x = kSzLoads * kThreads + tid; x < sz_seg; x += kThreads) {   // large K only
-            ls[x] = load16(rs, sz_base + (uint32_t)x * 16u, 0);
-            lz[x] = load16(rz, sz_base + (uint32_t)x * 16u, 0);
         }
     }
     if (tid < kBlockM)
         s_dst[tid] = tid < valid ? fid : -1;
+    if constexpr (NCH > 1) {
+#pragma unroll
+        for (int u = 0; u < P; ++u)
+            issue_w(u, u);
+    }
     __syncthreads();
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -595,30 +636,39 @@ __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, i
 #pragma unroll
     for (int ms = 0; ms < NMS; ++ms)
         dst[ms] = s_dst[ms * 16 + lrow];
-    f32x4 out[RT][NMS];
-
-    // ---- 2. stream this wave's row tiles, as straight-line code
+    f32x4 out[kDnTilesPerWave][NMS];
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
-        const int st = j % P;
+    for (int j = 0; j < kDnTilesPerWave; ++j)
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            out[j][ms] = zero4;
+
+    // ---- 3. stream this wave's units, as straight-line code
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int st = u % P;
+        const int j = u / NCH, c = u % NCH;
         // the activation reads are the same for every tile: an opaque offset
         // keeps the compiler from holding all of them in registers
         int aoff = 0;
         asm volatile("" : "+v"(aoff));
-        const int srow = min(tile_row(j) - rt0 * 16, max(0, rows_part - 16));   // first row in lds_s/lds_z
+        const int srow = min(tile_row(j) - rt0 * 16, max(0, nrt * 16 - 16));   // first row in lds_s/lds_z
 #pragma unroll
-        for (int ms = 0; ms < NMS; ++ms)
-            out[j][ms] = zero4;
-#pragma unroll
-        for (int g = 0; g < NGC; ++g) {
-            const int gc = min(g, NG - 1);
+        for (int g = 0; g < CH; ++g) {
+            const int gi = c * CH + g;
+            const int gc = min(gi, NG - 1);
             f16x2 c1024, c64;
-            zero_point_consts(lds_z[(srow + lrow) * NG + gc], c1024, c64);
+            zero_point_consts(lds_z[gc * kDnRows + srow + lrow], c1024, c64);
+            const uint2 s4 = *reinterpret_cast<const uint2 *>(lds_s + gc * kDnRows + srow + quarter * 4);
             float sc[4];
+            sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)s4.x);
+            sc[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(s4.x >> 16));
+            sc[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)s4.y);
+            sc[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(s4.y >> 16));
+            if (gi >= NG) {                       // a masked group of a rounded-up chunk
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float v = (float)__builtin_bit_cast(_Float16, lds_s[(srow + quarter * 4 + i) * NG + gc]);
-                sc[i] = g < NG ? v : 0.0f;
+                for (int i = 0; i < 4; ++i)
+                    sc[i] = 0.0f;
             }
             f32x4 prt[NMS];
 #pragma unroll
@@ -637,71 +687,513 @@ __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, i
                 for (int i = 0; i < 4; ++i)
                     out[j][ms][i] += sc[i] * prt[ms][i];
             // pin the accumulation here: otherwise the compiler sinks every
-            // tile's multiply-adds to the stores and keeps all partials live
+            // unit's multiply-adds to the stores and keeps all partials live
 #pragma unroll
             for (int ms = 0; ms < NMS; ++ms)
                 asm volatile("" : "+v"(out[j][ms]));
         }
-        issue_w(st, j + P);
+        issue_w(st, u + P);
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- 3. outputs: fp32 Y at each assignment's flat slot, one 16-byte
+    // ---- 4. outputs: fp16 Y at each assignment's flat slot, one 8-byte
     // store per assignment row and tile
-    float *Y = static_cast<float *>(p.out);
+    uint16_t *Y = static_cast<uint16_t *>(p.out);
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
+    for (int j = 0; j < kDnTilesPerWave; ++j) {
         if (!tile_live(j))
             continue;
         const int col = tile_row(j) + quarter * 4;
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms)
             if (dst[ms] >= 0)
-                *reinterpret_cast<f32x4 *>(Y + (size_t)dst[ms] * n_out + col) = out[j][ms];
+                *reinterpret_cast<uint2 *>(Y + (size_t)dst[ms] * n_out + col) = pack_f16x4(out[j][ms]);
     }
 }
 
-template <int G, class S>
-__global__ void __launch_bounds__(S::kWaves * 64)
-__attribute__((amdgpu_waves_per_eu(S::kWpe))) down_kernel(GemmArgs p, int parts)
+// Kernel entry for one (tile, column block): the tile's activation rows and
+// assignment ids are requested before its descriptor is known (they depend
+// only on the tile index), then the body for its row count runs.
+template <int G, int CH, int NCH, bool EXACT>
+__device__ __forceinline__ void down_entry(const GemmArgs &p, int tile, int cb)
 {
-    // workgroup -> (part, tile), XCD-aware as in gate_up
+    const int tid = threadIdx.x;
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)p.K * 2u);
+    uint4 av[kALoads];
+#pragma unroll
+    for (int i = 0; i < kALoads; ++i)
+        av[i] = load16(ra, down_a_off(p, tile * kBlockM, i * kDnThreads + tid), 0);
+    int fid = 0;
+    if (tid < kBlockM)
+        fid = p.sorted_ids[tile * kBlockM + tid];
+    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    if (info.x < 0)
+        return;
+    if (info.y > 16)
+        down_body<G, 2, CH, NCH, EXACT>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+    else
+        down_body<G, 1, CH, NCH, EXACT>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kDnThreads)
+__attribute__((amdgpu_waves_per_eu(4))) down_kernel(GemmArgs p)
+{
+    // workgroup -> (column block, tile), XCD-aware as in gate_up
+    const int nblocks = (p.n_out / 16 + kDnRows / 16 - 1) / (kDnRows / 16);
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    const int part = slot % parts;
-    const int tile = slot / parts * kXcds + xcd;
+    const int cb = slot % nblocks;
+    const int tile = slot / nblocks * kXcds + xcd;
     if (tile >= p.max_tiles)
         return;
+    const int ng = p.K / G;
+    // the layer's 11 groups of 64 as one chunk; otherwise chunks of 768 K
+    // (12 groups of 64 or 6 of 128), one or two of them
+    constexpr int kCh = 768 / G;
+    if constexpr (G == 64) {
+        if (ng == kDnGroups) {
+            down_entry<G, kDnGroups, 1, true>(p, tile, cb);
+            return;
+        }
+    }
+    if (ng <= kCh)
+        down_entry<G, kCh, 1, false>(p, tile, cb);
+    else
+        down_entry<G, kCh, 2, false>(p, tile, cb);
+}
+
+// ===========================================================================
+// Layer-shape kernels (d = 2816, m = 704, gate_up g = 128, down g = 64).
+//
+// Activation rows re-read from L2 share each CU's vector-memory path with the
+// weight stream, so these kernels cover wide column blocks per workgroup (the
+// activations are staged once per 352 gate_up columns and once per 1408 down
+// columns) and launch one 11-wave workgroup per CU: 2 per 32-row tile, 256
+// for the 128 tiles of a T = 256 canvas, a single round with one prologue.
+
+// ---- gate_up: workgroup = (tile, 352 output columns); wave w owns pairs 2w
+// and 2w + 1 (columns col0 + 32 w .. + 32) and computes them one after the
+// other: pass 0 walks all of K for pair 2w, pass 1 for pair 2w + 1. The 22
+// line steps run as straight-line code with the loads P steps ahead across
+// the pass boundary; each pass restages the same activation slices.
+constexpr int kL4Waves = 11;
+constexpr int kL4Threads = kL4Waves * 64;
+constexpr int kGu4Cols = kL4Waves * 32;          // 352
+constexpr int kGu4Ahead = 3;                     // weight steps in flight per wave
+constexpr int kGu4Rows = 2 * kGu4Cols;           // gate + up weight rows of a workgroup
+constexpr int kGu4Groups = kGuSteps * 2;         // 22 groups of 128
+
+constexpr int kGu4XRows = kBlockM + 1;          // row 32 takes the writes of rows past the tile
+constexpr int kGu4SzSeg = (kGu4Rows * kGu4Groups * 2 / 16 + kL4Threads - 1) / kL4Threads * kL4Threads;
+
+constexpr size_t gate_up4_lds_bytes()
+{
+    return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg;
+}
+
+template <int NMS>
+__device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
+                                              const int (&fidr)[2])
+{
+    constexpr int G = 128;
+    constexpr int P = kGu4Ahead;
+    constexpr int PX = 2;                          // activation stages, issued P - 1 steps ahead
+    constexpr int SG = 2;                          // groups per line step
+    constexpr int kWords = 4;
+    constexpr int NG = kGu4Groups;
+    constexpr int K = kGuSteps * 256;
+    constexpr int NQ = 2 * kGuSteps;               // line steps of both passes
+    constexpr int XLD = 2;                         // 32 rows x 32 segments over 704 threads
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15;
+    const int quarter = lane >> 4;
+    const int n_out = p.n_out;
+    const size_t wexp = (size_t)e * p.n_w;
+    const int col0 = cb * kGu4Cols;
+
+    extern __shared__ uint4 lds[];
+    uint4 *lds_x = lds;                                             // [2][33][kStepPitch]
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kGu4XRows * kStepPitch);   // [704 rows][NG]
+    uint16_t *lds_z = lds_s + kGu4SzSeg * 8;
+
+    // ---- 1. scale/zero of the 352 gate and 352 up rows, then per step the
+    // activations and the weights (in issue order: row ids, scale/zero,
+    // then step by step)
+    const uint32_t sz_bytes = (uint32_t)p.n_w * (uint32_t)NG * 2u;
+    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, sz_bytes);
+    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, sz_bytes);
+    constexpr int kRangeSeg = kGu4Cols * NG / 8;   // 968 segments per 352-row range
+    constexpr int kSzLoads = (2 * kRangeSeg + kL4Threads - 1) / kL4Threads;   // 3
+    auto sz_off = [&](int x) -> uint32_t {
+        if (x >= 2 * kRangeSeg)
+            return kOutOfRange;
+        const int r = x >= kRangeSeg;
+        return (uint32_t)(((r ? n_out : 0) + col0) * NG) * 2u + (uint32_t)(x - r * kRangeSeg) * 16u;
+    };
+    uint4 sv[kSzLoads], zv[kSzLoads];
+#pragma unroll
+    for (int i = 0; i < kSzLoads; ++i) {
+        const uint32_t off = sz_off(i * kL4Threads + tid);
+        sv[i] = load16(rs, off, 0);
+        zv[i] = load16(rz, off, 0);
+    }
+
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
+    // pass c: gate rows col0 + 32 wave + 16 c + lrow, then the matching up rows
+    auto in_range = [&](int c) { return wave * 32 + c * 16 + lrow; };
+    auto wvoff = [&](int c, int u) {
+        return (uint32_t)((u ? n_out : 0) + col0 + in_range(c)) * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8));
+    };
+    Frag<G> bq[P][2][SG];
+    auto issue_w = [&](int st, int q) {            // global step q = 11 pass + step
+        const int c = q / kGuSteps, s = q % kGuSteps;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t voff = wvoff(c, u);
+#pragma unroll
+            for (int h = 0; h < SG; ++h)
+                bq[st][u][h] = load_frag<G>(rq, voff, (uint32_t)((s * SG + h) * (G / 2)));
+        }
+    };
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
+    const int xseg = tid % kStepSeg;
+    uint32_t xoff[XLD];
+#pragma unroll
+    for (int i = 0; i < XLD; ++i) {
+        const int r = (i * kL4Threads + tid) / kStepSeg;
+        xoff[i] = r < NMS * 16 && fidr[i] < p.A
+                      ? (uint32_t)(fidr[i] / p.topk) * (uint32_t)K * 2u + (uint32_t)xseg * 16u
+                      : kOutOfRange;
+    }
+    uint4 xr[PX][XLD];
+    auto issue_x = [&](int st, int q) {
+        const int s = q % kGuSteps;
+#pragma unroll
+        for (int i = 0; i < XLD; ++i)
+            xr[st][i] = load16(ra, xoff[i] != kOutOfRange ? xoff[i] + (uint32_t)s * 512u : kOutOfRange, 0);
+    };
+    // prologue: x(0) w(0) x(1) w(1) w(2); in step q: x(q + PX) then w(q + P),
+    // so waiting for a step's activations never waits for later weights
+    issue_x(0, 0);
+    issue_w(0, 0);
+#pragma unroll
+    for (int q = 1; q < P; ++q) {
+        if (q < PX)
+            issue_x(q, q);
+        issue_w(q, q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. scale/zero into LDS (made visible by the first step's barrier;
+    // the segments past the rows land in the area's rounded-up tail)
+    {
+        uint4 *ls = reinterpret_cast<uint4 *>(lds_s);
+        uint4 *lz = reinterpret_cast<uint4 *>(lds_z);
+        static_assert(kSzLoads * kL4Threads == kGu4SzSeg, "scale/zero area");
+#pragma unroll
+        for (int i = 0; i < kSzLoads; ++i) {
+            ls[i * kL4Threads + tid] = sv[i];
+            lz[i * kL4Threads + tid] = zv[i];
+        }
+    }
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    uint16_t *H = static_cast<uint16_t *>(p.out);
+
+    // ---- 3. two passes of 11 line steps, straight-line
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int lds_row0 = in_range(c);                 // gate row in lds_s/lds_z
+        const int lds_row1 = kGu4Cols + in_range(c);      // up row
+        f32x4 acc[2][NMS];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms)
+                acc[u][ms] = zero4;
+#pragma unroll
+        for (int s = 0; s < kGuSteps; ++s) {
+            const int q = c * kGuSteps + s;
+            const int st = q % P;
+            uint4 *xb = lds_x + (q & 1) * kGu4XRows * kStepPitch;
+#pragma unroll
+            for (int i = 0; i < XLD; ++i) {
+                const int r = min((i * kL4Threads + tid) / kStepSeg, kBlockM);
+                xb[r * kStepPitch + xseg] = permute8(xr[q % PX][i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            // an opaque LDS offset per step keeps the compiler from hoisting
+            // later steps' scale/zero and activation reads into registers
+            int loff = 0;
+            asm volatile("" : "+v"(loff));
+#pragma unroll
+            for (int h = 0; h < SG; ++h) {
+                const int gi = s * SG + h;
+                float scale[2];
+                f16x2 c1024[2], c64[2];
+                zero_point_consts(lds_z[loff + lds_row0 * NG + gi], c1024[0], c64[0]);
+                zero_point_consts(lds_z[loff + lds_row1 * NG + gi], c1024[1], c64[1]);
+                scale[0] = (float)__builtin_bit_cast(_Float16, lds_s[loff + lds_row0 * NG + gi]);
+                scale[1] = (float)__builtin_bit_cast(_Float16, lds_s[loff + lds_row1 * NG + gi]);
+                f32x4 part[2][NMS];
+#pragma unroll
+                for (int t = 0; t < kWords; ++t) {
+                    f16x8 bop[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        bop[u] = dequant8(frag_word<G>(bq[st][u][h], t), c1024[u], c64[u]);
+                    const int seg = h * (G / 8) + quarter * (G / 32) + t;
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms) {
+                        const f16x8 aop = __builtin_bit_cast(f16x8, xb[loff + (ms * 16 + lrow) * kStepPitch + seg]);
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            part[u][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                aop, bop[u], t == 0 ? zero4 : part[u][ms], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[u][ms][i] += scale[u] * part[u][ms][i];
+                        // pin the accumulation here: otherwise the compiler
+                        // sinks it to the epilogue and keeps every partial live
+                        asm volatile("" : "+v"(acc[u][ms]));
+                    }
+            }
+            if (q + PX < NQ)
+                issue_x(q % PX, q + PX);
+            if (q + P < NQ)
+                issue_w(st, q + P);
+        }
+        // epilogue of the pass: H = gelu_tanh(gate) * up in fp16, permuted per 8
+        const int col = col0 + in_range(c);
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = ms * 16 + quarter * 4 + i;
+                if (r >= valid)
+                    continue;
+                const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
+                H[(size_t)(row0 + r) * n_out + permuted_col(col)] = __builtin_bit_cast(uint16_t, (_Float16)h);
+            }
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kL4Threads) gate_up4_kernel(GemmArgs p)
+{
+    // workgroup -> (column half, tile); both halves of a tile on one XCD
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int cb = slot % 2;
+    const int tile = slot / 2 * kXcds + xcd;
+    if (tile >= p.max_tiles)
+        return;
+    const int tid = threadIdx.x;
+    int fidr[2];
+    fidr[0] = p.sorted_ids[tile * kBlockM + tid / kStepSeg];               // rows 0..21
+    fidr[1] = p.sorted_ids[tile * kBlockM + min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];   // rows 22..31
+    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    if (info.x < 0)
+        return;
+    if (info.y > 16)
+        gate_up4_body<2>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+    else
+        gate_up4_body<1>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+}
+
+// ---- down: workgroup = (tile, 1408 output columns = 88 row tiles); wave w
+// streams row tiles w, w + 11, ..., w + 77 (the 11 waves read neighbouring
+// tiles at any time), P tiles ahead, each tile's output stored when done.
+constexpr int kDn4Tiles = 8;                     // row tiles per wave
+constexpr int kDn4Rows = kL4Waves * kDn4Tiles * 16;   // 1408 weight rows per workgroup
+constexpr int kDn4Ahead = 2;
+constexpr int kDn4ALoads = 4;                    // 32 rows x 88 segments over 704 threads
+
+constexpr size_t down4_lds_bytes()
+{
+    return sizeof(uint4) * kBlockM * (kDnGroups * 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * kDnGroups;
+}
+
+template <int NMS>
+__device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
+                                           const uint4 (&av)[kDn4ALoads], int fid)
+{
+    constexpr int G = 64;
+    constexpr int P = kDn4Ahead;
+    constexpr int NG = kDnGroups;
+    constexpr int K = NG * G;                      // 704
+    constexpr int kWords = 2;
+    constexpr int a_pitch = K / 8 + 1;
+    constexpr int seg_row = K / 8;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15;
+    const int quarter = lane >> 4;
+    const int n_out = p.n_out;
+    const size_t wexp = (size_t)e * p.n_w;
+    const int rt0 = cb * (kDn4Rows / 16);          // first weight row tile of the block
+
+    extern __shared__ uint4 lds[];
+    uint4 *lds_a = lds;                                             // [32][a_pitch]
+    uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + kBlockM * a_pitch);   // [NG][1408]
+    uint16_t *lds_z = lds_s + kDn4Rows * NG;
+    __shared__ int s_dst[kBlockM];
+
+    // ---- 1. scale/zero of the block's rows, then the first weight tiles
+    const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
+    constexpr int kSzSeg = kDn4Rows * NG * 2 / 16;                  // 1936
+    constexpr int kSzLoads = (kSzSeg + kL4Threads - 1) / kL4Threads;   // 3
+    const uint32_t sz_base = (uint32_t)(rt0 * 16 * NG) * 2u;
+    uint4 sv[kSzLoads], zv[kSzLoads];
+#pragma unroll
+    for (int i = 0; i < kSzLoads; ++i) {
+        const int x = i * kL4Threads + tid;
+        const uint32_t off = x < kSzSeg ? sz_base + (uint32_t)x * 16u : kOutOfRange;
+        sv[i] = load16(rs, off, 0);
+        zv[i] = load16(rz, off, 0);
+    }
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
+    auto tile_row = [&](int j) { return (rt0 + wave + j * kL4Waves) * 16; };   // first weight row
+    Frag<G> bq[P][NG];
+    auto issue_w = [&](int st, int j) {
+        const uint32_t voff = j < kDn4Tiles ? (uint32_t)(tile_row(j) + lrow) * (uint32_t)(K / 2) +
+                                                  (uint32_t)(quarter * (G / 8))
+                                            : kOutOfRange;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            bq[st][g] = load_frag<G>(rq, voff, (uint32_t)(g * (G / 2)));
+    };
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        issue_w(j, j);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. activations, scale/zero (transposed to [g][row]) and row
+    // destinations into LDS
+#pragma unroll
+    for (int i = 0; i < kDn4ALoads; ++i) {
+        const int x = i * kL4Threads + tid;
+        const int r = x / seg_row, sg = x - r * seg_row;
+        if (r < 16 * NMS)
+            lds_a[r * a_pitch + sg] = av[i];
+    }
+    {
+        auto put8 = [&](uint16_t *dst, int x, uint4 v) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int el = x * 8 + k;
+                const int r = el / NG, g = el - r * NG;
+                dst[g * kDn4Rows + r] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < kSzLoads; ++i) {
+            const int x = i * kL4Threads + tid;
+            if (x < kSzSeg) {
+                put8(lds_s, x, sv[i]);
+                put8(lds_z, x, zv[i]);
+            }
+        }
+    }
+    if (tid < kBlockM)
+        s_dst[tid] = fid < p.A ? fid : -1;
+    __syncthreads();
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    int dst[NMS];
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+        dst[ms] = s_dst[ms * 16 + lrow];
+    uint16_t *Y = static_cast<uint16_t *>(p.out);
+
+    // ---- 3. stream the wave's 8 row tiles, P ahead; each tile's 16 x 32
+    // outputs are stored as soon as its 11 groups are done
+#pragma unroll
+    for (int j = 0; j < kDn4Tiles; ++j) {
+        const int st = j % P;
+        int aoff = 0;                              // keeps the A reads per tile (see gate_up)
+        asm volatile("" : "+v"(aoff));
+        const int srow = tile_row(j) - rt0 * 16;
+        f32x4 out[NMS];
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            out[ms] = zero4;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            asm volatile("" : "+v"(aoff));         // and per group: no hoisting of later groups' reads
+            f16x2 c1024, c64;
+            zero_point_consts(lds_z[g * kDn4Rows + srow + lrow], c1024, c64);
+            const uint2 s4 = *reinterpret_cast<const uint2 *>(lds_s + g * kDn4Rows + srow + quarter * 4);
+            float sc[4];
+            sc[0] = (float)__builtin_bit_cast(_Float16, (uint16_t)s4.x);
+            sc[1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(s4.x >> 16));
+            sc[2] = (float)__builtin_bit_cast(_Float16, (uint16_t)s4.y);
+            sc[3] = (float)__builtin_bit_cast(_Float16, (uint16_t)(s4.y >> 16));
+            f32x4 prt[NMS];
+#pragma unroll
+            for (int t = 0; t < kWords; ++t) {
+                const f16x8 bop = dequant8(frag_word<G>(bq[st][g], t), c1024, c64);
+                const int seg = g * (G / 8) + quarter * (G / 32) + t;
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+                    const f16x8 aop = __builtin_bit_cast(f16x8, lds_a[aoff + (ms * 16 + lrow) * a_pitch + seg]);
+                    prt[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop, aop, t == 0 ? zero4 : prt[ms], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[ms][i] += sc[i] * prt[ms][i];
+                asm volatile("" : "+v"(out[ms]));   // pin the accumulation (see gate_up)
+            }
+        }
+        issue_w(st, j + P);
+        const int col = tile_row(j) + quarter * 4;
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            if (dst[ms] >= 0)
+                *reinterpret_cast<uint2 *>(Y + (size_t)dst[ms] * n_out + col) = pack_f16x4(out[ms]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
+{
+    // workgroup -> (column half, tile), both halves of a tile on one XCD; the
+    // tile's activation rows and assignment ids are requested before its
+    // descriptor is known
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int cb = slot % 2;
+    const int tile = slot / 2 * kXcds + xcd;
+    if (tile >= p.max_tiles)
+        return;
+    const int tid = threadIdx.x;
+    const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)p.K * 2u);
+    uint4 av[kDn4ALoads];
+#pragma unroll
+    for (int i = 0; i < kDn4ALoads; ++i)
+        av[i] = load16(ra, down_a_off(p, tile * kBlockM, i * kL4Threads + tid), 0);
+    int fid = p.A;
+    if (tid < kBlockM)
+        fid = p.sorted_ids[tile * kBlockM + tid];
     const int2 info = p.tile_info[tile];
     if (info.x < 0)
         return;
-    const int ng = p.K / G;
-    // group counts with an instantiation: the layer's (11 groups of 64), else
-    // the next of 12 / 24 groups of 64 (6 / 12 of 128) with idle groups masked
-    constexpr int kSmall = 768 / G, kLarge = 1536 / G;
-    if (G == 64 && ng == kDnGroups) {
-        if (info.y > 16)
-            down_body<G, S, 2, kDnGroups>(p, info.x, info.y, tile * kBlockM, part);
-        else
-            down_body<G, S, 1, kDnGroups>(p, info.x, info.y, tile * kBlockM, part);
-    } else if (ng <= kSmall) {
-        if (info.y > 16)
-            down_body<G, S, 2, kSmall>(p, info.x, info.y, tile * kBlockM, part);
-        else
-            down_body<G, S, 1, kSmall>(p, info.x, info.y, tile * kBlockM, part);
-    } else {
-        if (info.y > 16)
-            down_body<G, S, 2, kLarge>(p, info.x, info.y, tile * kBlockM, part);
-        else
-            down_body<G, S, 1, kLarge>(p, info.x, info.y, tile * kBlockM, part);
-    }
-}
-
-template <int G, class S>
-size_t down_lds_bytes(int K)
-{
-    const size_t part_rows = (size_t)S::kWaves * S::kTiles * 16;
-    return sizeof(uint4) * kBlockM * ((size_t)K / 8 + 1) +
-           2 * sizeof(uint16_t) * part_rows * (size_t)(K / G);
+    if (info.y > 16)
+        down4_body<2>(p, info.x, tile * kBlockM, cb, av, fid);
+    else
+        down4_body<1>(p, info.x, tile * kBlockM, cb, av, fid);
 }
 
 template <class Kern>
@@ -716,40 +1208,70 @@ hipError_t allow_lds(Kern kern, size_t lds, size_t &allowed)
     return err;
 }
 
+// the layer's shape takes the wide-block kernels
+bool layer_shape_gate_up(const GemmArgs &a, int g)
+{
+    return g == 128 && a.K == kGuSteps * 256 && a.n_out == 2 * kGu4Cols && a.n_w == 2 * a.n_out;
+}
+
+bool layer_shape_down(const GemmArgs &a, int g)
+{
+    return g == 64 && a.K == kDnGroups * 64 && a.n_out == 2 * kDn4Rows && a.n_w == a.n_out;
+}
+
+hipError_t launch_gate_up4(const GemmArgs &a, hipStream_t stream)
+{
+    static size_t allowed = 64 * 1024;
+    hipError_t err = allow_lds(gate_up4_kernel, gate_up4_lds_bytes(), allowed);
+    if (err != hipSuccess)
+        return err;
+    const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
+    gate_up4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), gate_up4_lds_bytes(), stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
+{
+    static size_t allowed = 64 * 1024;
+    hipError_t err = allow_lds(down4_kernel, down4_lds_bytes(), allowed);
+    if (err != hipSuccess)
+        return err;
+    const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
+    down4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes(), stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_gate_up_g(const GemmArgs &a, hipStream_t stream)
 {
-    using S = GateUpShape;
-    constexpr int cols_per_wg = S::kWaves * S::kTiles / 2 * 16;
-    const int nblocks = (a.n_out + cols_per_wg - 1) / cols_per_wg;
+    const int nblocks = (a.n_out + kGuCols - 1) / kGuCols;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    auto kern = gate_up_kernel<G, S>;
+    auto kern = gate_up_kernel<G>;
     static size_t allowed = 64 * 1024;              // raised once per instantiation when needed
-    const size_t lds = gate_up_lds_bytes<G, S>(a.K);
+    const size_t lds = gate_up_lds_bytes_k<G>(a.K);
     hipError_t err = allow_lds(kern, lds, allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
-    kern<<<dim3(tiles * nblocks), dim3(S::kWaves * 64), lds, stream>>>(a);
+    kern<<<dim3(tiles * nblocks), dim3(kGuThreads), lds, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int G>
 hipError_t launch_down_g(const GemmArgs &a, hipStream_t stream)
 {
-    using S = DownShape;
-    if (a.max_tiles == 0)
+    const int nblocks = (a.n_out / 16 + kDnRows / 16 - 1) / (kDnRows / 16);
+    if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    const int parts = (a.n_out / 16 + S::kWaves * S::kTiles - 1) / (S::kWaves * S::kTiles);
-    auto kern = down_kernel<G, S>;
+    auto kern = down_kernel<G>;
     static size_t allowed = 64 * 1024;
-    const size_t lds = down_lds_bytes<G, S>(a.K);
+    const size_t lds = down_lds_bytes_k<G>(a.K);
     hipError_t err = allow_lds(kern, lds, allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
-    kern<<<dim3(tiles * parts), dim3(S::kWaves * 64), lds, stream>>>(a, parts);
+    kern<<<dim3(tiles * nblocks), dim3(kDnThreads), lds, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -758,19 +1280,29 @@ hipError_t launch_down_g(const GemmArgs &a, hipStream_t stream)
 size_t gemm_lds_bytes(bool gated, int K, int g)
 {
     if (gated)
-        return g == 128 ? gate_up_lds_bytes<128, GateUpShape>(K) : gate_up_lds_bytes<64, GateUpShape>(K);
-    return g == 128 ? down_lds_bytes<128, DownShape>(K) : down_lds_bytes<64, DownShape>(K);
+        return g == 128 ? gate_up_lds_bytes_k<128>(K) : gate_up_lds_bytes_k<64>(K);
+    return g == 128 ? down_lds_bytes_k<128>(K) : down_lds_bytes_k<64>(K);
 }
 
 int down_max_k() { return 1536; }
 
+int gate_up_max_groups() { return kGuMaxGroups; }
+
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
+    if (a.max_tiles == 0)
+        return hipSuccess;
+    if (layer_shape_gate_up(a, g))
+        return launch_gate_up4(a, stream);
     return g == 128 ? launch_gate_up_g<128>(a, stream) : launch_gate_up_g<64>(a, stream);
 }
 
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
 {
+    if (a.max_tiles == 0)
+        return hipSuccess;
+    if (layer_shape_down(a, g))
+        return launch_down4(a, stream);
     return g == 128 ? launch_down_g<128>(a, stream) : launch_down_g<64>(a, stream);
 }
 
