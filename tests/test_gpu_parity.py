@@ -181,6 +181,14 @@ def test_forward_full_deterministic_100(full_layer):
     assert bad == 0
 
 
+def test_forward_layer_shape_unfused_sampled():
+    # gate_up with g=64 at the layer's shape: the generic gate_up kernel, then
+    # the layer-shape down kernel as a launch of its own
+    shp = lc.custom_shape("unfused", E=128, topk=8, T=256, d=2816, m=704, g_gu=64, index=91)
+    L = lc.build(shp)
+    _sampled(L, 16, 4, "layer shape, gate_up g=64 (sampled 16 tokens)")
+
+
 def test_forward_skew_sampled():
     L = lc.build(CONFIGS["skew"])
     _sampled(L, 16, 2, "skew(sampled 16 tokens)")

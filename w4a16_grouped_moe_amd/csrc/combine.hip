@@ -12,6 +12,11 @@
 // 8-byte loads of Y, one 8-byte store. Every output element is produced by
 // exactly one thread with a fixed sequence of operations, so the result is
 // bitwise reproducible.
+//
+// The kernel is bound by load latency, not bandwidth (11.5 MB of Y spread over
+// the whole chip is one round of loads per thread), so for topk = 8 all ids,
+// weights and Y loads of a thread are issued before the first addition; a
+// token's row of d/4 threads is one workgroup when it fits.
 #include "dgw4_internal.hpp"
 
 #pragma clang fp contract(off)
@@ -49,6 +54,47 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint2 *__restrict__ 
     out[(size_t)t * d4 + c4] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
 }
 
+// topk fixed at compile time: every load is in flight before the first add.
+// The Y slot of a skipped k exists (it is simply not written by the GEMMs), so
+// it is loaded like the others and left out of the sum.
+template <int K>
+__global__ void __launch_bounds__(1024) combine_fixed_kernel(const uint2 *__restrict__ y,
+                                                             const int32_t *__restrict__ ids,
+                                                             const float *__restrict__ w, int E,
+                                                             int d4, uint2 *__restrict__ out)
+{
+    const int t = blockIdx.y;
+    const int c4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c4 >= d4)
+        return;
+    int e[K];
+    float wk[K];
+    uint2 v[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        e[k] = ids[(size_t)t * K + k];
+        wk[k] = w[(size_t)t * K + k];
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+        v[k] = y[((size_t)t * K + k) * d4 + c4];
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        if (e[k] < 0 || e[k] >= E)
+            continue;
+        a0 = __fadd_rn(a0, __fmul_rn(wk[k], h2f(v[k].x & 0xFFFFu)));
+        a1 = __fadd_rn(a1, __fmul_rn(wk[k], h2f(v[k].x >> 16)));
+        a2 = __fadd_rn(a2, __fmul_rn(wk[k], h2f(v[k].y & 0xFFFFu)));
+        a3 = __fadd_rn(a3, __fmul_rn(wk[k], h2f(v[k].y >> 16)));
+    }
+    const uint32_t h0 = __builtin_bit_cast(uint16_t, (_Float16)a0);
+    const uint32_t h1 = __builtin_bit_cast(uint16_t, (_Float16)a1);
+    const uint32_t h2 = __builtin_bit_cast(uint16_t, (_Float16)a2);
+    const uint32_t h3 = __builtin_bit_cast(uint16_t, (_Float16)a3);
+    out[(size_t)t * d4 + c4] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+}
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
@@ -57,6 +103,14 @@ hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const floa
     if (T == 0)
         return hipSuccess;
     const int d4 = d / 4;
+    if (topk == 8) {
+        // one workgroup per token row when it fits, whole waves
+        const int threads = d4 <= 1024 ? (d4 + 63) / 64 * 64 : 256;
+        const dim3 grid((d4 + threads - 1) / threads, T);
+        combine_fixed_kernel<8><<<grid, dim3(threads), 0, stream>>>(
+            reinterpret_cast<const uint2 *>(y), topk_ids, topk_w, E, d4, reinterpret_cast<uint2 *>(out));
+        return hipGetLastError();
+    }
     const dim3 grid((d4 + 255) / 256, T);
     combine_kernel<<<grid, dim3(256), 0, stream>>>(reinterpret_cast<const uint2 *>(y), topk_ids,
                                                    topk_w, topk, E, d4,

@@ -30,11 +30,11 @@ int from_hip(hipError_t e)
     return DGW4_ERR_HIP;
 }
 
-// Workspace of one forward call: alignment buffers, x in the GEMM's K order,
-// the gated intermediate H (fp16, one row per padded assignment) and the
+// Workspace of one forward call: alignment buffers, per-tile counters of the
+// fused GEMM launch, the gated intermediate H (fp16, one row per padded assignment) and the
 // per-assignment expert outputs Y (fp16, one row per flat assignment id).
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, ready, sorted_ids, h, y, total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap)
@@ -51,6 +51,7 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
+    L.ready = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take(sizeof(uint16_t) * (size_t)A * (size_t)d);
@@ -119,7 +120,7 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_align(topk_ids, T * topk, E, block_m, (long long)cap, counts,
                                        offsets, sorted_ids, tile_expert, num_padded, nullptr,
-                                       (hipStream_t)stream));
+                                       nullptr, 0, (hipStream_t)stream));
 }
 
 int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
@@ -185,6 +186,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
     int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
+    int32_t *ready = reinterpret_cast<int32_t *>(ws + L.ready);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
@@ -192,42 +194,52 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     hipError_t err = mark(0);
     if (err == hipSuccess)
         err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
-                                 offsets, sorted_ids, tile_expert, num_padded, tile_info, st);
+                                 offsets, sorted_ids, tile_expert, num_padded, tile_info, ready,
+                                 (int)(cap / dgw4::kBlockM), st);
     if (err == hipSuccess)
         err = mark(1);
     if (err != hipSuccess)
         return from_hip(err);
 
-    dgw4::GemmArgs g{};
-    g.sorted_ids = sorted_ids;
-    g.tile_info = tile_info;
-    g.topk = topk;
-    g.A = (int)A;
-    g.max_tiles = (int)(cap / dgw4::kBlockM);
+    dgw4::GemmArgs gu{};
+    gu.sorted_ids = sorted_ids;
+    gu.tile_info = tile_info;
+    gu.topk = topk;
+    gu.A = (int)A;
+    gu.max_tiles = (int)(cap / dgw4::kBlockM);
+    dgw4::GemmArgs dn = gu;
 
-    g.a_src = x;
-    g.a_rows = T;
-    g.q = gu_q;
-    g.s = gu_s;
-    g.z = gu_z;
-    g.K = d;
-    g.n_w = 2 * m;
-    g.n_out = m;
-    g.out = h;
-    if ((err = dgw4::launch_gate_up(g, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
-        return from_hip(err);
+    gu.a_src = x;
+    gu.a_rows = T;
+    gu.q = gu_q;
+    gu.s = gu_s;
+    gu.z = gu_z;
+    gu.K = d;
+    gu.n_w = 2 * m;
+    gu.n_out = m;
+    gu.out = h;
 
-    g.a_src = h;
-    g.a_rows = (int)cap;
-    g.q = dn_q;
-    g.s = dn_s;
-    g.z = dn_z;
-    g.K = m;
-    g.n_w = d;
-    g.n_out = d;
-    g.out = y;
-    if ((err = dgw4::launch_down(g, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
-        return from_hip(err);
+    dn.a_src = h;
+    dn.a_rows = (int)cap;
+    dn.q = dn_q;
+    dn.s = dn_s;
+    dn.z = dn_z;
+    dn.K = m;
+    dn.n_w = d;
+    dn.n_out = d;
+    dn.out = y;
+
+    if (dgw4::gate_up_down_fused(gu, gu_g, dn, dn_g)) {
+        // one launch for both GEMMs: the stage marks 2 and 3 both follow it
+        if ((err = dgw4::launch_gate_up_down(gu, dn, ready, st)) != hipSuccess ||
+            (err = mark(2)) != hipSuccess || (err = mark(3)) != hipSuccess)
+            return from_hip(err);
+    } else {
+        if ((err = dgw4::launch_gate_up(gu, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
+            return from_hip(err);
+        if ((err = dgw4::launch_down(dn, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
+            return from_hip(err);
+    }
 
     if ((err = dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st)) != hipSuccess ||
         (err = mark(4)) != hipSuccess)

@@ -22,10 +22,12 @@ hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t 
 // Alignment of the flat assignment ids to experts (one workgroup per
 // expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
 // the tile that hold assignments} for live tiles, {-1, 0} past the total.
+// ready (may be null) gets n_ready zeros: the per-tile counters of the fused
+// gate_up + down launch that follows.
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
-                        hipStream_t stream);
+                        int32_t *ready, int n_ready, hipStream_t stream);
 
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
@@ -55,6 +57,12 @@ struct GemmArgs {
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
+
+// Whether the pair of GEMMs runs as one launch (the layer's shape), and that
+// launch: ready holds one zeroed counter per tile (gu.max_tiles of them).
+bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g);
+hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
+                               hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
                           int T, int topk, int E, int d, uint16_t *out, hipStream_t stream);

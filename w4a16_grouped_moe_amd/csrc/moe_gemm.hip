@@ -37,8 +37,8 @@
 //
 // Activation rows re-read from L2 share each CU's vector-memory path with the
 // weight stream and measurably lower it, so the layer's shape (d = 2816,
-// m = 704, gate_up g = 128, down g = 64) takes wide-block kernels launched as
-// one 11-wave workgroup per CU (2 per 32-row tile, 256 for the 128 tiles of a
+// m = 704, gate_up g = 128, down g = 64) takes wide-block bodies run as one
+// 11-wave workgroup per CU (2 per 32-row tile, 256 for the 128 tiles of a
 // 256-token canvas):
 //   gate_up4: workgroup = (tile, 352 output columns); wave w owns pairs 2w and
 //     2w + 1 (16 gate columns and the matching up columns each) and computes
@@ -49,6 +49,14 @@
 //     tile's activations (all of K = 704) and the block's scales/zero points
 //     are staged in LDS once; wave w streams row tiles w, w + 11, ..., 2 tiles
 //     ahead, storing each tile's fp16 outputs as soon as it is done.
+//   layer4_kernel runs both in one launch: workgroup (tile, half) does gate_up4
+//     for its half of H, raises the tile's counter, prefetches its down
+//     weights and waits for the partner half before reading H. This removes
+//     the second launch, its ramp-up and the gate_up tail. H crosses CUs at
+//     device scope (write-through stores, device-scope loads) rather than
+//     through device-scope fences, which would write back and invalidate the
+//     whole L2 of an XCD each time.
+// down4 also runs alone when gate_up has another group size.
 // Other shapes take the generic kernels:
 //   gate_up_kernel: workgroup = (tile, 64 columns), 4 waves, one pair each.
 //   down_kernel: workgroup = (tile, 256 columns), 8 waves, two row tiles each,
@@ -81,6 +89,15 @@ __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes)
 __device__ inline uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// The same load at device scope (cache policy sc1): it is served coherently
+// for the whole device, so it sees stores that other CUs made at device scope
+// without any cache invalidation.
+constexpr int kCpolDevice = 16;
+__device__ inline uint4 load16_device(rsrc_t r, uint32_t voff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolDevice));
 }
 
 template <int G>
@@ -776,6 +793,23 @@ __attribute__((amdgpu_waves_per_eu(4))) down_kernel(GemmArgs p)
 // other: pass 0 walks all of K for pair 2w, pass 1 for pair 2w + 1. The 22
 // line steps run as straight-line code with the loads P steps ahead across
 // the pass boundary; each pass restages the same activation slices.
+// Polls of a counter that another workgroup of the same launch raises; the
+// bound (about 2^16 polls of a microsecond or less) only guarantees that the
+// kernel ends if the counter never gets there.
+constexpr int kSpinLimit = 1 << 16;
+
+// One lane waits until *flag >= target (device-scope loads); the rest of the
+// workgroup follows through a barrier, and the data the counter announces is
+// then read with device-scope loads.
+__device__ __noinline__ void wait_count(const int32_t *flag, int target)
+{
+    for (int i = 0; i < kSpinLimit; ++i) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target)
+            break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 constexpr int kL4Waves = 11;
 constexpr int kL4Threads = kL4Waves * 64;
 constexpr int kGu4Cols = kL4Waves * 32;          // 352
@@ -791,6 +825,8 @@ constexpr size_t gate_up4_lds_bytes()
     return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg;
 }
 
+// H is stored at device scope (written through to memory): its consumer is
+// the down half of the same launch, on another CU.
 template <int NMS>
 __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                               const int (&fidr)[2])
@@ -981,31 +1017,12 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
                 if (r >= valid)
                     continue;
                 const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
-                H[(size_t)(row0 + r) * n_out + permuted_col(col)] = __builtin_bit_cast(uint16_t, (_Float16)h);
+                uint16_t *dst = H + (size_t)(row0 + r) * n_out + permuted_col(col);
+                const uint16_t bits = __builtin_bit_cast(uint16_t, (_Float16)h);
+                __hip_atomic_store(dst, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-}
-
-__global__ void __launch_bounds__(kL4Threads) gate_up4_kernel(GemmArgs p)
-{
-    // workgroup -> (column half, tile); both halves of a tile on one XCD
-    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    const int cb = slot % 2;
-    const int tile = slot / 2 * kXcds + xcd;
-    if (tile >= p.max_tiles)
-        return;
-    const int tid = threadIdx.x;
-    int fidr[2];
-    fidr[0] = p.sorted_ids[tile * kBlockM + tid / kStepSeg];               // rows 0..21
-    fidr[1] = p.sorted_ids[tile * kBlockM + min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];   // rows 22..31
-    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
-    if (info.x < 0)
-        return;
-    if (info.y > 16)
-        gate_up4_body<2>(p, info.x, info.y, tile * kBlockM, cb, fidr);
-    else
-        gate_up4_body<1>(p, info.x, info.y, tile * kBlockM, cb, fidr);
 }
 
 // ---- down: workgroup = (tile, 1408 output columns = 88 row tiles); wave w
@@ -1021,9 +1038,11 @@ constexpr size_t down4_lds_bytes()
     return sizeof(uint4) * kBlockM * (kDnGroups * 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * kDnGroups;
 }
 
-template <int NMS>
+// FUSED: H of the tile is produced in the same launch; av is loaded here
+// once `ready` shows both halves, after the weight prefetch is under way.
+template <int NMS, bool FUSED>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
-                                           const uint4 (&av)[kDn4ALoads], int fid)
+                                           uint4 (&av)[kDn4ALoads], int fid, const int32_t *ready)
 {
     constexpr int G = 64;
     constexpr int P = kDn4Ahead;
@@ -1077,15 +1096,8 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
         issue_w(j, j);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 2. activations, scale/zero (transposed to [g][row]) and row
+    // ---- 2. scale/zero (transposed to [g][row]), activations and row
     // destinations into LDS
-#pragma unroll
-    for (int i = 0; i < kDn4ALoads; ++i) {
-        const int x = i * kL4Threads + tid;
-        const int r = x / seg_row, sg = x - r * seg_row;
-        if (r < 16 * NMS)
-            lds_a[r * a_pitch + sg] = av[i];
-    }
     {
         auto put8 = [&](uint16_t *dst, int x, uint4 v) {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -1104,6 +1116,22 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
                 put8(lds_z, x, zv[i]);
             }
         }
+    }
+    if constexpr (FUSED) {
+        if (tid == 0)
+            wait_count(ready, 2);
+        __syncthreads();
+        const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
+#pragma unroll
+        for (int i = 0; i < kDn4ALoads; ++i)
+            av[i] = load16_device(ra, down_a_off(p, row0, i * kL4Threads + tid));
+    }
+#pragma unroll
+    for (int i = 0; i < kDn4ALoads; ++i) {
+        const int x = i * kL4Threads + tid;
+        const int r = x / seg_row, sg = x - r * seg_row;
+        if (r < 16 * NMS)
+            lds_a[r * a_pitch + sg] = av[i];
     }
     if (tid < kBlockM)
         s_dst[tid] = fid < p.A ? fid : -1;
@@ -1191,9 +1219,60 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     if (info.x < 0)
         return;
     if (info.y > 16)
-        down4_body<2>(p, info.x, tile * kBlockM, cb, av, fid);
+        down4_body<2, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr);
     else
-        down4_body<1>(p, info.x, tile * kBlockM, cb, av, fid);
+        down4_body<1, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr);
+}
+
+// ---- gate_up and down of the layer's shape in one launch. Workgroup (tile,
+// column half) runs gate_up4 for its half of H, announces it on the tile's
+// counter, then runs down4 for its half of the outputs once both halves of H
+// are there. The two halves of a tile are neighbours in dispatch order on
+// one XCD, so a workgroup only ever waits for a partner that is resident or
+// next in line, and H stays in that XCD's L2. The counters start at zero
+// (the alignment step clears them) and the wait is bounded.
+constexpr size_t layer4_lds_bytes()
+{
+    return gate_up4_lds_bytes() > down4_lds_bytes() ? gate_up4_lds_bytes() : down4_lds_bytes();
+}
+
+__global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArgs dn, int32_t *ready)
+{
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int cb = slot % 2;
+    const int tile = slot / 2 * kXcds + xcd;
+    if (tile >= gu.max_tiles)
+        return;
+    const int tid = threadIdx.x;
+    int fidr[2];
+    fidr[0] = gu.sorted_ids[tile * kBlockM + tid / kStepSeg];
+    fidr[1] = gu.sorted_ids[tile * kBlockM + min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];
+    const int2 info = gu.tile_info[tile];
+    if (info.x < 0)
+        return;
+    if (info.y > 16)
+        gate_up4_body<2>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
+    else
+        gate_up4_body<1>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
+
+    // this half of H is written at device scope: once every wave has seen its
+    // stores complete, one device-scope add announces the half. (Device-scope
+    // fences would write back and invalidate the whole L2 of the XCD, which
+    // stalls every other workgroup streaming through it.)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+        __hip_atomic_fetch_add(ready + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    int fid = dn.A;
+    if (tid < kBlockM)
+        fid = dn.sorted_ids[tile * kBlockM + tid];
+    uint4 av[kDn4ALoads];
+    if (info.y > 16)
+        down4_body<2, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile);
+    else
+        down4_body<1, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile);
 }
 
 template <class Kern>
@@ -1208,7 +1287,7 @@ hipError_t allow_lds(Kern kern, size_t lds, size_t &allowed)
     return err;
 }
 
-// the layer's shape takes the wide-block kernels
+// the layer's shape takes the wide-block kernels (gate_up only fused with down)
 bool layer_shape_gate_up(const GemmArgs &a, int g)
 {
     return g == 128 && a.K == kGuSteps * 256 && a.n_out == 2 * kGu4Cols && a.n_w == 2 * a.n_out;
@@ -1219,17 +1298,6 @@ bool layer_shape_down(const GemmArgs &a, int g)
     return g == 64 && a.K == kDnGroups * 64 && a.n_out == 2 * kDn4Rows && a.n_w == a.n_out;
 }
 
-hipError_t launch_gate_up4(const GemmArgs &a, hipStream_t stream)
-{
-    static size_t allowed = 64 * 1024;
-    hipError_t err = allow_lds(gate_up4_kernel, gate_up4_lds_bytes(), allowed);
-    if (err != hipSuccess)
-        return err;
-    const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
-    gate_up4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), gate_up4_lds_bytes(), stream>>>(a);
-    return hipGetLastError();
-}
-
 hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;
@@ -1238,6 +1306,17 @@ hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
         return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
     down4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes(), stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer4(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready, hipStream_t stream)
+{
+    static size_t allowed = 64 * 1024;
+    hipError_t err = allow_lds(layer4_kernel, layer4_lds_bytes(), allowed);
+    if (err != hipSuccess)
+        return err;
+    const int tiles = (gu.max_tiles + kXcds - 1) / kXcds * kXcds;
+    layer4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), layer4_lds_bytes(), stream>>>(gu, dn, ready);
     return hipGetLastError();
 }
 
@@ -1292,8 +1371,6 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
     if (a.max_tiles == 0)
         return hipSuccess;
-    if (layer_shape_gate_up(a, g))
-        return launch_gate_up4(a, stream);
     return g == 128 ? launch_gate_up_g<128>(a, stream) : launch_gate_up_g<64>(a, stream);
 }
 
@@ -1304,6 +1381,19 @@ hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
     if (layer_shape_down(a, g))
         return launch_down4(a, stream);
     return g == 128 ? launch_down_g<128>(a, stream) : launch_down_g<64>(a, stream);
+}
+
+bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g)
+{
+    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g);
+}
+
+hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
+                               hipStream_t stream)
+{
+    if (gu.max_tiles == 0)
+        return hipSuccess;
+    return launch_layer4(gu, dn, ready, stream);
 }
 
 }  // namespace dgw4
