@@ -50,12 +50,15 @@
 //     are staged in LDS once; wave w streams row tiles w, w + 11, ..., 2 tiles
 //     ahead, storing each tile's fp16 outputs as soon as it is done.
 //   layer4_kernel runs both in one launch: workgroup (tile, half) does gate_up4
-//     for its half of H, raises the tile's counter, prefetches its down
-//     weights and waits for the partner half before reading H. This removes
-//     the second launch, its ramp-up and the gate_up tail. H crosses CUs at
-//     device scope (write-through stores, device-scope loads) rather than
-//     through device-scope fences, which would write back and invalidate the
-//     whole L2 of an XCD each time.
+//     for its half of H (gathered in LDS, stored in 16-byte segments),
+//     requests its down scales/zeros and first weight tiles, raises the
+//     tile's counter once its H stores are complete and waits for the
+//     partner half before reading H. This removes the second launch, its
+//     ramp-up and the gate_up tail. H crosses CUs at device scope
+//     (write-through stores, device-scope loads) rather than through
+//     device-scope fences, which would write back and invalidate the whole L2
+//     of an XCD each time. The store acknowledgement still costs one memory
+//     round trip under full load (several microseconds) per workgroup.
 // down4 also runs alone when gate_up has another group size.
 // Other shapes take the generic kernels:
 //   gate_up_kernel: workgroup = (tile, 64 columns), 4 waves, one pair each.
@@ -74,6 +77,7 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int kXcds = 8;                          // accelerator dies (each with its own L2) on MI355X
@@ -820,13 +824,17 @@ constexpr int kGu4Groups = kGuSteps * 2;         // 22 groups of 128
 constexpr int kGu4XRows = kBlockM + 1;          // row 32 takes the writes of rows past the tile
 constexpr int kGu4SzSeg = (kGu4Rows * kGu4Groups * 2 / 16 + kL4Threads - 1) / kL4Threads * kL4Threads;
 
+constexpr int kGu4HSeg = kGu4Cols * 2 / 16;      // 16-byte segments of one H row half (44)
+
 constexpr size_t gate_up4_lds_bytes()
 {
-    return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg;
+    return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg +
+           sizeof(uint4) * kBlockM * kGu4HSeg;
 }
 
-// H is stored at device scope (written through to memory): its consumer is
-// the down half of the same launch, on another CU.
+// H is gathered in LDS and stored at device scope (written through to
+// memory) in whole 16-byte segments: its consumer is the down half of the
+// same launch, on another CU.
 template <int NMS>
 __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                               const int (&fidr)[2])
@@ -853,6 +861,7 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
     uint4 *lds_x = lds;                                             // [2][33][kStepPitch]
     uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kGu4XRows * kStepPitch);   // [704 rows][NG]
     uint16_t *lds_z = lds_s + kGu4SzSeg * 8;
+    uint16_t *lds_h = lds_z + kGu4SzSeg * 8;                       // [32 rows][352] H, permuted per 8
 
     // ---- 1. scale/zero of the 352 gate and 352 up rows, then per step the
     // activations and the weights (in issue order: row ids, scale/zero,
@@ -935,7 +944,6 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
         }
     }
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    uint16_t *H = static_cast<uint16_t *>(p.out);
 
     // ---- 3. two passes of 11 line steps, straight-line
 #pragma unroll
@@ -1007,21 +1015,34 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
             if (q + P < NQ)
                 issue_w(st, q + P);
         }
-        // epilogue of the pass: H = gelu_tanh(gate) * up in fp16, permuted per 8
-        const int col = col0 + in_range(c);
+        // epilogue of the pass: H = gelu_tanh(gate) * up in fp16, permuted per
+        // 8, into the LDS tile (each wave owns its columns)
+        const int hcol = permuted_col(in_range(c));       // col0 is a multiple of 8
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ms * 16 + quarter * 4 + i;
-                if (r >= valid)
-                    continue;
                 const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
-                uint16_t *dst = H + (size_t)(row0 + r) * n_out + permuted_col(col);
-                const uint16_t bits = __builtin_bit_cast(uint16_t, (_Float16)h);
-                __hip_atomic_store(dst, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lds_h[r * kGu4Cols + hcol] = __builtin_bit_cast(uint16_t, (_Float16)h);
             }
         }
+    }
+
+    // ---- 4. the valid rows of the H tile to memory, 16 bytes per store
+    __syncthreads();
+    const rsrc_t rh = make_rsrc(p.out, (uint32_t)(p.max_tiles * kBlockM) * (uint32_t)n_out * 2u);
+    const uint4 *lh = reinterpret_cast<const uint4 *>(lds_h);
+    constexpr int kHStores = (kBlockM * kGu4HSeg + kL4Threads - 1) / kL4Threads;   // 2
+#pragma unroll
+    for (int i = 0; i < kHStores; ++i) {
+        const int x = i * kL4Threads + tid;
+        const int r = x / kGu4HSeg, sg = x - r * kGu4HSeg;
+        const uint32_t off = r < valid ? (uint32_t)(row0 + r) * (uint32_t)n_out * 2u + (uint32_t)col0 * 2u +
+                                             (uint32_t)sg * 16u
+                                       : kOutOfRange;
+        const uint4 v = lh[min(x, kBlockM * kGu4HSeg - 1)];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rh, off, 0, kCpolDevice);
     }
 }
 
@@ -1038,11 +1059,21 @@ constexpr size_t down4_lds_bytes()
     return sizeof(uint4) * kBlockM * (kDnGroups * 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * kDnGroups;
 }
 
-// FUSED: H of the tile is produced in the same launch; av is loaded here
-// once `ready` shows both halves, after the weight prefetch is under way.
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone
+constexpr int vmcnt_at_most(int n)
+{
+    return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+// FUSED: this workgroup has just issued its half of H (device-scope stores)
+// in the same launch. The scale/zero and first weight loads go out first;
+// then, once only those loads can still be outstanding, the stores are
+// complete and the half is announced; av is loaded once the counter shows
+// both halves.
 template <int NMS, bool FUSED>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
-                                           uint4 (&av)[kDn4ALoads], int fid, const int32_t *ready)
+                                           uint4 (&av)[kDn4ALoads], int fid, int32_t *ready)
 {
     constexpr int G = 64;
     constexpr int P = kDn4Ahead;
@@ -1095,6 +1126,18 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     for (int j = 0; j < P; ++j)
         issue_w(j, j);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FUSED) {
+        // vector memory operations issued since the H stores: scale/zero, weights
+        constexpr int kIssued = 2 * kSzLoads + P * NG;
+        static_assert(kIssued < 64, "vmcnt range");
+        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kIssued));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();                           // also: every wave is done with gate_up's LDS
+        if (tid == 0) {
+            __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            wait_count(ready, 2);
+        }
+    }
 
     // ---- 2. scale/zero (transposed to [g][row]), activations and row
     // destinations into LDS
@@ -1118,9 +1161,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
         }
     }
     if constexpr (FUSED) {
-        if (tid == 0)
-            wait_count(ready, 2);
-        __syncthreads();
+        __syncthreads();                           // lane 0 has seen both halves
         const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
 #pragma unroll
         for (int i = 0; i < kDn4ALoads; ++i)
@@ -1247,6 +1288,9 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
     int fidr[2];
     fidr[0] = gu.sorted_ids[tile * kBlockM + tid / kStepSeg];
     fidr[1] = gu.sorted_ids[tile * kBlockM + min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];
+    int fid = dn.A;                                // down's row destination, for later
+    if (tid < kBlockM)
+        fid = dn.sorted_ids[tile * kBlockM + tid];
     const int2 info = gu.tile_info[tile];
     if (info.x < 0)
         return;
@@ -1254,20 +1298,11 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
         gate_up4_body<2>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
     else
         gate_up4_body<1>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
-
-    // this half of H is written at device scope: once every wave has seen its
-    // stores complete, one device-scope add announces the half. (Device-scope
-    // fences would write back and invalidate the whole L2 of the XCD, which
-    // stalls every other workgroup streaming through it.)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-        __hip_atomic_fetch_add(ready + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
-    int fid = dn.A;
-    if (tid < kBlockM)
-        fid = dn.sorted_ids[tile * kBlockM + tid];
+    // nothing but the down body's own loads may follow the H stores before
+    // it announces the half (it counts them); device-scope fences are not
+    // used for that: they would write back and invalidate the whole L2 of
+    // the XCD, stalling every other workgroup streaming through it
+    __builtin_amdgcn_sched_barrier(0);
     uint4 av[kDn4ALoads];
     if (info.y > 16)
         down4_body<2, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile);
