@@ -56,7 +56,7 @@ def layer_bytes(shape, populated: int) -> dict:
     )
 
 
-TRAFFIC_PROFILE = "profiles/moe_gemm_T256_hbm_traffic.md"
+TRAFFIC_PROFILE = "profiles/layer4_T256_hbm_traffic.md"
 TRAFFIC_SOURCES = ("w4a16_grouped_moe_amd/csrc/moe_gemm.hip",
                    "w4a16_grouped_moe_amd/csrc/dgw4_internal.hpp")
 
