@@ -31,8 +31,10 @@ HBM_PEAK_GBPS = 8000.0
 # with the measured machine"): 2.366 ms. As GB/s on this layer's algorithmic
 # bytes it is context from another machine, not a target.
 GB10_LAYER_MS = 2.366
-# Steps of the separate pass that splits a step into its stages (see main()).
+# Steps of the separate pass that splits a step into its stages, and sweeps
+# of the rotated stack for the spread and the graph replay (see main()).
 STAGE_STEPS = 300
+SWEEPS = 20
 
 
 def log(*a):
@@ -88,6 +90,64 @@ def measured_traffic() -> dict | None:
     if rec.get("source_sha256") != gemm_source_hash():
         return None
     return rec
+
+
+def graph_replay(torch, dg, step, L, R, out, last, ws, dev) -> dict:
+    """Capture one sweep of L layer forwards into a HIP graph, replay it R
+    times, and compare the last layer's output with an eager forward."""
+    stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)              # default priority
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(L):
+            step(i)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            step(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+    ev[0].record(stream)
+    for r in range(R):
+        g.replay()
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([ev[r].elapsed_time(ev[r + 1]) * 1e3 / L for r in range(R)])
+    replayed = out.clone()
+    eager = dg.moe_forward(last["x"], last["ids"], last["w"], last["gu"], last["dn"], workspace=ws)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(replayed.view(torch.int16), eager.view(torch.int16)))
+    del g
+    return {"replays": R, "layers_per_replay": L,
+            "median_us_per_layer": round(float(np.median(us)), 2),
+            "p10_us_per_layer": round(float(np.percentile(us, 10)), 2),
+            "p90_us_per_layer": round(float(np.percentile(us, 90)), 2),
+            "bitwise_equal_to_eager": same}
+
+
+def read_probe(torch, dg, dev, gib: int = 2, reps: int = 10) -> dict:
+    """On-box HBM read ceiling: the library's whole-chip read of a `gib` GiB
+    buffer (8x the 256 MB Infinity Cache, so it streams from HBM)."""
+    n = gib << 30
+    buf = torch.ones(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        dg.hbm_read_probe(buf, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dg.hbm_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    return {"kind": f"whole-chip read of a {gib} GiB buffer (dgw4_hbm_read_probe)",
+            "gbps": round(gbps, 1)}
 
 
 def cpu_baseline(shape):
@@ -199,6 +259,28 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
 
+    # Spread: R sweeps of the rotated stack, each bracketed by events (a pass
+    # of its own, so the timed steps above carry no events).
+    R = SWEEPS
+    sw = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+    torch.cuda.synchronize()
+    sw[0].record(stream)
+    for r in range(R):
+        for i in range(L):
+            step(i)
+        sw[r + 1].record(stream)
+    torch.cuda.synchronize()
+    sweep_us = np.array([sw[r].elapsed_time(sw[r + 1]) * 1e3 / L for r in range(R)])
+    spread = {"sweeps": R, "layers_per_sweep": L,
+              "median_us_per_layer": round(float(np.median(sweep_us)), 2),
+              "p10_us_per_layer": round(float(np.percentile(sweep_us, 10)), 2),
+              "p90_us_per_layer": round(float(np.percentile(sweep_us, 90)), 2)}
+
+    # The same sweep replayed as one HIP graph (captured once; every replay
+    # re-runs alignment and both GEMMs on the device), checked bitwise
+    # against the eager result of its last layer.
+    graph = graph_replay(torch, dg, step, L, R, out, layers[L - 1], ws, dev)
+
     # Stage split, in a pass of its own after the timed region: each recorded
     # event adds a few microseconds of dispatch gap, so they stay out of the
     # steps that give the throughput. The layer's shape runs gate_up and down
@@ -226,6 +308,8 @@ def main() -> int:
         f"{gbps:.1f} GB/s ({100 * gbps / HBM_PEAK_GBPS:.1f}% of 8 TB/s)")
     log(f"[bench] stages over {S} steps (us): {stage_us}; gate_up+down launch {gemm_gbps:.1f} GB/s")
 
+    probe = read_probe(torch, dg, dev)
+    probe["pct_of_probe"] = round(100 * gbps / probe["gbps"], 2)
     traffic = measured_traffic()
     pages_gbps = layers[0]["bytes"]["layer"] / (GB10_LAYER_MS * 1e-3) / 1e9
     result = {
@@ -260,6 +344,9 @@ def main() -> int:
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_layer": layers[0]["bytes"]["layer"],
         "stage_us": stage_us,
+        "eager_sweeps": spread,
+        "graph_replay": graph,
+        "hbm_probe": probe,
         "roofline": {
             "kernel": "layer4_kernel (gate_up + GELU(tanh) gate + down in one launch, layer shape)",
             "bound": "hbm",

@@ -172,9 +172,11 @@ DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const 
  * timing of the same launch sequence (same kernels, same arguments, same
  * results). events is an array of n_events = 5 caller-created hipEvent_t
  * handles (passed as void*); they are recorded on `stream` before the
- * alignment kernel and after each of the four kernels (align, gate_up, down,
+ * alignment kernel and after each of the four stages (align, gate_up, down,
  * combine). Elapsed time between consecutive events is the duration of one
- * stage. events == NULL behaves exactly like dgw4_moe_forward; any other
+ * stage. Where gate_up and down run as one launch (d = 2816, m = 704,
+ * gate_up g = 128, down g = 64), events 2 and 3 are both recorded after that
+ * launch and the down stage brackets no kernel. events == NULL behaves exactly like dgw4_moe_forward; any other
  * n_events is DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL)
  * records nothing.
  */
@@ -185,6 +187,19 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
                                     void *workspace, size_t *ws_bytes, uint16_t *out,
                                     void *stream, void *const *events, int n_events);
+
+/*
+ * dgw4_hbm_read_probe — a measurement aid, not a step of the layer: reads
+ * `bytes` bytes of device memory at `buf` once, with the whole chip
+ * (16-byte loads, several in flight per lane), so that the elapsed time on
+ * `stream` gives the read bandwidth this device sustains. The loads are
+ * folded into one word, stored to sink[0] only if it equals 0x9E3779B9
+ * (never, for a buffer filled with one repeated byte), which keeps them from
+ * being optimised away. buf: device memory, 16-byte aligned; bytes: a
+ * positive multiple of 16; sink: device memory of at least 4 bytes.
+ * Returns DGW4_ERR_INVALID_ARG otherwise, DGW4_ERR_HIP if the launch fails.
+ */
+DGW4_API int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

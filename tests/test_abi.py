@@ -94,3 +94,15 @@ def test_align_rejects():
     assert a(None, 4, 2, 8, 32, p, p, p, p, p, None) == B.ERR_INVALID_ARG
     assert a(p, 4, 2, 8, 32, p, None, p, p, p, None) == B.ERR_INVALID_ARG
     assert a(p, -1, 2, 8, 32, p, p, p, p, p, None) == B.ERR_INVALID_ARG
+
+
+def test_read_probe_rejects():
+    # checked on the host before any launch: null pointers, sizes that are
+    # not a positive multiple of 16, misaligned buffers
+    r = dg.lib().dgw4_hbm_read_probe
+    p = 1 << 12
+    assert r(None, 16, p, None) == B.ERR_INVALID_ARG
+    assert r(p, 16, None, None) == B.ERR_INVALID_ARG
+    assert r(p, 0, p, None) == B.ERR_INVALID_ARG
+    assert r(p, 24, p, None) == B.ERR_INVALID_ARG
+    assert r(p + 8, 16, p, None) == B.ERR_INVALID_ARG

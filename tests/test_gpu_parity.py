@@ -189,6 +189,35 @@ def test_forward_layer_shape_unfused_sampled():
     _sampled(L, 16, 4, "layer shape, gate_up g=64 (sampled 16 tokens)")
 
 
+def test_forward_graph_replay_matches_eager(full_layer):
+    # the forward enqueues kernels only (no host sync, no memset), so it can be
+    # captured; every replay re-aligns and clears its tile counters on the
+    # device, so replays after scribbling on the workspace stay bitwise equal
+    L = full_layer
+    ws = torch.empty(dg.workspace_bytes(L.shape.T, L.shape.topk, L.shape.E, L.shape.d,
+                                        L.shape.m), dtype=torch.uint8, device="cuda")
+    ref = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=ws).clone()
+    out = torch.empty_like(ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=ws, out=out)
+    for r in range(4):
+        out.zero_()
+        ws.random_(0, 256)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        lc.log(f"[graph] replay {r}")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r} differs"
+    del g
+
+
 def test_forward_skew_sampled():
     L = lc.build(CONFIGS["skew"])
     _sampled(L, 16, 2, "skew(sampled 16 tokens)")

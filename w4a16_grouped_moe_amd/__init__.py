@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     Dgw4Error,
     align,
     align_capacity,
+    hbm_read_probe,
     header_functions,
     lib,
     moe_forward,

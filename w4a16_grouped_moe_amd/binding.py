@@ -63,6 +63,8 @@ def lib():
                                              P, P, P, I, P, P, P, I,
                                              P, ctypes.POINTER(S), P, P,
                                              ctypes.POINTER(P), I]
+        L.dgw4_hbm_read_probe.restype = I
+        L.dgw4_hbm_read_probe.argtypes = [P, S, P, P]
         _lib = L
     return _lib
 
@@ -155,6 +157,16 @@ def workspace_bytes(T: int, topk: int, E: int, d: int, m: int, gu_g: int = 128,
         None, None, None, T, topk, E, d, m, None, None, None, gu_g, None, None, None, dn_g,
         None, ctypes.byref(n), None, None))
     return int(n.value)
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
+    """Enqueue one whole-chip read of ``buf`` (a measurement aid: time it
+    with events on the current stream). ``buf`` device uint8, size a multiple
+    of 16; ``sink`` device int32 with at least one element."""
+    pb = _dev(buf, "buf", (torch.uint8,))
+    ps = _dev(sink, "sink", (torch.int32,))
+    _check("dgw4_hbm_read_probe",
+           lib().dgw4_hbm_read_probe(pb, buf.numel(), ps, _stream(buf)))
 
 
 STAGES = ("align", "gate_up", "down", "combine")

@@ -258,4 +258,11 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
                                   nullptr, 0);
 }
 
+int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16))
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

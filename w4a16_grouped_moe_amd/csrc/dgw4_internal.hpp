@@ -64,6 +64,10 @@ bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn
 hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
                                hipStream_t stream);
 
+// One read of `bytes` (a multiple of 16) at buf over the whole chip; see
+// dgw4_hbm_read_probe.
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
                           int T, int topk, int E, int d, uint16_t *out, hipStream_t stream);
 
