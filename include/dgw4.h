@@ -191,7 +191,7 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
 /*
  * dgw4_hbm_read_probe — a measurement aid, not a step of the layer: reads
  * `bytes` bytes of device memory at `buf` once, with the whole chip
- * (16-byte loads, several in flight per lane), so that the elapsed time on
+ * (16-byte non-temporal loads, several in flight per lane), so that the elapsed time on
  * `stream` gives the read bandwidth this device sustains. The loads are
  * folded into one word, stored to sink[0] only if it equals 0x9E3779B9
  * (never, for a buffer filled with one repeated byte), which keeps them from
