@@ -150,6 +150,55 @@ def read_probe(torch, dg, dev, gib: int = 2, reps: int = 10) -> dict:
             "gbps": round(gbps, 1)}
 
 
+def bench_linear(torch, dg, dev, args) -> int:
+    """The dense W4A16 linear at an LM-head shape: x fp16 [256, 2816] against
+    one packed [262144, 2816] matrix (392 MB of nibbles, scales and zeros:
+    more than the 256 MB Infinity Cache, so it streams from HBM on every
+    call). Prints one JSON line of its own."""
+    from synth import linear_inputs
+    T, K, N, g = 256, 2816, 262144, 128
+    x, _ = linear_inputs(5, T, K, 16)
+    xd = torch.from_numpy(x).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    wd = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32).mul_(0.02)
+    q, s_, z = dg.quantize_rtn(wd, g)
+    del wd
+    y = torch.empty((T, N), dtype=torch.float16, device=dev)
+    w = (q, s_, z, g)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(1, args.warmup // 30)):
+        dg.w4a16_linear(xd, w, out=y)
+    steps = max(1, args.steps // 30)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        dg.w4a16_linear(xd, w, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    wbytes = N * K // 2 + 2 * N * (K // g) * 2
+    nbytes = wbytes + T * K * 2 + T * N * 2
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"[linear] {steps} calls: {ms * 1e3:.1f} us each, {gbps:.1f} GB/s")
+    print(json.dumps({
+        "metric": "us per dense W4A16 linear + achieved HBM GB/s (% of 8 TB/s)",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": max(1, args.warmup // 30), "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"dense W4A16 linear (LM-head shape): T={T}, K={K}, N={N}, g={g}"},
+        "us_per_call": round(ms * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "bytes_per_call": nbytes,
+        "roofline": {"kernel": "linear_kernel<128>", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def cpu_baseline(shape):
     """The CPU oracle, as it stands, on one full layer drawn on the host."""
     import oracle
@@ -181,7 +230,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3000, help="timed layer forwards")
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--layers", type=int, default=30, help="distinct weight sets in rotation")
-    ap.add_argument("--workload", default="stack", choices=["stack", "full", "skew", "wide"])
+    ap.add_argument("--workload", default="stack", choices=["stack", "full", "skew", "wide", "lmhead"],
+                    help="lmhead: the dense W4A16 linear at T=256, K=2816, N=262144 (not the layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 5 times (the counter "
@@ -212,6 +262,8 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"[copy] 5 copies of {n} bytes")
         return 0
+    if args.workload == "lmhead":
+        return bench_linear(torch, dg, dev, args)
     shape = CONFIGS[args.workload]
     L = args.layers if args.workload == "stack" else 1
     if args.workload != "stack":

@@ -189,6 +189,26 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     void *stream, void *const *events, int n_events);
 
 /*
+ * dgw4_w4a16_linear — the dense W4A16 linear layer: y = x * deq(W)^T
+ * ([kcard] "W4A16": w4a16_linear(x, qw, scale, zero) equals F.linear(x,
+ * dequant(W)); the same packing and the same GEMM core as the routed-expert
+ * layer, one weight matrix, every row of x).
+ *   x  fp16 [T, K] row-major, 16-byte aligned;
+ *   q  uint8 [N, K/2], s and z fp16 [N, K/g]: one matrix in the layout of
+ *      dgw4_quantize_rtn with E = 1 (16-byte aligned);
+ *   y  fp16 [T, N] row-major (written, caller-owned).
+ * Each output is the fp32 sum over K of x times (q - z) with the group's
+ * scale applied once per group in fp32, rounded once to fp16.
+ * Returns DGW4_ERR_INVALID_ARG for null pointers (T > 0), negative T, odd K,
+ * K % g != 0 or misaligned pointers; DGW4_ERR_UNSUPPORTED for g not in
+ * {64, 128}, N not a multiple of 16, more than 64 groups per row, or tensors
+ * past 2 GiB. T == 0 is a no-op. Enqueued on `stream`, no host sync.
+ */
+DGW4_API int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
+                               const uint16_t *s, const uint16_t *z, int g, uint16_t *y,
+                               void *stream);
+
+/*
  * dgw4_hbm_read_probe — a measurement aid, not a step of the layer: reads
  * `bytes` bytes of device memory at `buf` once, with the whole chip
  * (16-byte non-temporal loads, several in flight per lane), so that the elapsed time on

@@ -14,4 +14,5 @@ from .inputs import (  # noqa: F401
     activations,
     routing,
     zipf_prior,
+    linear_inputs,
 )

@@ -141,3 +141,13 @@ def routing(shape: LayerShape, layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
         tot[:, 0] += pk[:, k]
     w = (pk / tot).astype(np.float32)
     return ids, np.ascontiguousarray(w)
+
+
+def linear_inputs(seed: int, T: int, K: int, N: int, std: float = 0.02,
+                  threads: int = 8) -> tuple[np.ndarray, np.ndarray]:
+    """A dense layer's inputs: x fp16 [T, K] ~ N(0, 1) (rounded to nearest) and
+    the fp32 master weight [N, K] ~ N(0, std), each from its own child stream
+    of ``seed``."""
+    x = _normal_rows(seed * 2 + 1, T, K, 1.0, threads).astype(np.float16)
+    w = _normal_rows(seed * 2, N, K, std, threads)
+    return x, w

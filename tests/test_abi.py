@@ -106,3 +106,20 @@ def test_read_probe_rejects():
     assert r(p, 0, p, None) == B.ERR_INVALID_ARG
     assert r(p, 24, p, None) == B.ERR_INVALID_ARG
     assert r(p + 8, 16, p, None) == B.ERR_INVALID_ARG
+
+
+def test_linear_rejects():
+    # host-side checks before any launch
+    f = dg.lib().dgw4_w4a16_linear
+    p = 1 << 12
+    assert f(p, 4, 256, 64, p, p, p, 100, p, None) == B.ERR_UNSUPPORTED      # g
+    assert f(p, 4, 255, 64, p, p, p, 64, p, None) == B.ERR_INVALID_ARG       # odd K
+    assert f(p, 4, 320, 64, p, p, p, 128, p, None) == B.ERR_INVALID_ARG      # K % g
+    assert f(p, 4, 256, 40, p, p, p, 64, p, None) == B.ERR_UNSUPPORTED       # N % 16
+    assert f(p, 4, 64 * 65, 64, p, p, p, 64, p, None) == B.ERR_UNSUPPORTED   # > 64 groups
+    assert f(None, 4, 256, 64, p, p, p, 64, p, None) == B.ERR_INVALID_ARG
+    assert f(p, 4, 256, 64, p, p, p, 64, None, None) == B.ERR_INVALID_ARG
+    assert f(p, -1, 256, 64, p, p, p, 64, p, None) == B.ERR_INVALID_ARG
+    assert f(p + 8, 4, 256, 64, p, p, p, 64, p, None) == B.ERR_INVALID_ARG   # alignment
+    assert f(None, 0, 256, 64, None, None, None, 64, None, None) == B.OK     # T = 0: no-op
+

@@ -16,4 +16,5 @@ from .binding import (  # noqa: F401
     status_string,
     version,
     workspace_bytes,
+    w4a16_linear,
 )

@@ -63,6 +63,8 @@ def lib():
                                              P, P, P, I, P, P, P, I,
                                              P, ctypes.POINTER(S), P, P,
                                              ctypes.POINTER(P), I]
+        L.dgw4_w4a16_linear.restype = I
+        L.dgw4_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P, P]
         L.dgw4_hbm_read_probe.restype = I
         L.dgw4_hbm_read_probe.argtypes = [P, S, P, P]
         _lib = L
@@ -121,6 +123,29 @@ def quantize_rtn(w: torch.Tensor, g: int):
     _check("dgw4_quantize_rtn", lib().dgw4_quantize_rtn(
         pw, E, N, K, g, q.data_ptr(), s.data_ptr(), z.data_ptr(), _stream(w)))
     return q, s, z
+
+
+def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense W4A16 linear: y = x * deq(W)^T.
+
+    x fp16 [T, K]; w = (q uint8 [N, K/2], s fp16 [N, K/g], z fp16 [N, K/g], g),
+    e.g. one matrix of quantize_rtn. Returns y fp16 [T, N]."""
+    q, s, z, g = w
+    T, K = x.shape
+    N = q.shape[0]
+    if q.shape != (N, K // 2) or s.shape != (N, K // g) or z.shape != s.shape:
+        raise ValueError(f"packed shapes {tuple(q.shape)}, {tuple(s.shape)} do not match x {tuple(x.shape)}")
+    px = _dev(x, "x", _F16)
+    pq = _dev(q, "q", (torch.uint8,))
+    ps = _dev(s, "s", _F16)
+    pz = _dev(z, "z", _F16)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float16, device=x.device)
+    if out.shape != (T, N):
+        raise ValueError("out must be [T, N]")
+    py = _dev(out, "out", _F16)
+    _check("dgw4_w4a16_linear", lib().dgw4_w4a16_linear(px, T, K, N, pq, ps, pz, g, py, _stream(x)))
+    return out
 
 
 def align_capacity(T: int, topk: int, E: int, block_m: int) -> int:

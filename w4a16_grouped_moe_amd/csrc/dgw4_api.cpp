@@ -265,4 +265,42 @@ int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *str
     return from_hip(dgw4::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
 }
 
+int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
+                      const uint16_t *s, const uint16_t *z, int g, uint16_t *y, void *stream)
+{
+    if (T < 0 || K < 2 || (K % 2) != 0 || N < 1 || g < 1)
+        return DGW4_ERR_INVALID_ARG;
+    if (!group_supported(g))
+        return DGW4_ERR_UNSUPPORTED;
+    if (K % g != 0)
+        return DGW4_ERR_INVALID_ARG;
+    // the kernel covers column blocks of whole 16-column tiles, stages the
+    // scales of up to gate_up_max_groups() groups per row in LDS, and
+    // addresses x, y and W with 32-bit offsets
+    if (N % 16 != 0 || K / g > dgw4::gate_up_max_groups() ||
+        (long long)T * K * 2 >= (1LL << 31) || (long long)T * N * 2 >= (1LL << 31) ||
+        (long long)N * K / 2 >= (1LL << 31))
+        return DGW4_ERR_UNSUPPORTED;
+    if (T == 0)
+        return DGW4_OK;
+    if (!x || !q || !s || !z || !y)
+        return DGW4_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 16) || !aligned(z, 16) || !aligned(y, 2))
+        return DGW4_ERR_INVALID_ARG;
+    dgw4::GemmArgs a{};
+    a.a_src = x;
+    a.a_rows = T;
+    a.q = q;
+    a.s = s;
+    a.z = z;
+    a.K = K;
+    a.n_w = N;
+    a.n_out = N;
+    a.topk = 1;
+    a.A = T;
+    a.max_tiles = (T + dgw4::kBlockM - 1) / dgw4::kBlockM;
+    a.out = y;
+    return from_hip(dgw4::launch_linear(a, g, (hipStream_t)stream));
+}
+
 }  // extern "C"

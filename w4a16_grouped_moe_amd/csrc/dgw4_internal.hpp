@@ -56,6 +56,11 @@ struct GemmArgs {
 };
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
+
+// Dense linear y = x * deq(W)^T over the a.A = a_rows rows of x in order:
+// a.sorted_ids / a.tile_info unused, one weight matrix (n_w = n_out = N rows),
+// a.out = y fp16 [A, N] in natural column order.
+hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
 
 // Whether the pair of GEMMs runs as one launch (the layer's shape), and that

@@ -71,6 +71,8 @@
 // one 16-row MFMA block instead of two.
 #include "dgw4_internal.hpp"
 
+#include <climits>
+
 namespace dgw4 {
 namespace {
 
@@ -235,10 +237,14 @@ constexpr size_t gate_up_lds_bytes_k(int K)
 
 // NSC > 0: K = 256 NSC exactly, a compile-time constant, and the K loop is
 // fully unrolled; NSC = 0: a generic loop over ceil(K / 256) steps.
-template <int G, int NMS, int NSC>
+// GATED: each wave computes a gate column tile and the matching up tile and
+// stores gelu_tanh(gate) * up as H (permuted per 8); otherwise (the dense
+// linear) one column tile, stored as fp16 in natural column order.
+template <int G, int NMS, int NSC, bool GATED>
 __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                              const int (&fidr)[4])
 {
+    constexpr int TT = GATED ? 2 : 1;             // weight row tiles per wave
     constexpr int P = kGuAhead;                   // weights P steps ahead
     constexpr int PX = P - 1;                     // activations P - 1 steps ahead (L2 hits)
     constexpr int SG = 256 / G;                   // groups per line step
@@ -279,7 +285,7 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, sz_bytes);
     constexpr int kSzLoads = 4;                   // covers NG <= kGuMaxGroups
     const int range_seg = kGuCols * NG / 8;       // 16-byte segments per 64-row range
-    const int sz_total = 2 * range_seg;
+    const int sz_total = TT * range_seg;
     auto sz_off = [&](int x) -> uint32_t {
         if (x >= sz_total)
             return kOutOfRange;
@@ -297,18 +303,18 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2),
                                 live ? (uint32_t)p.n_w * (uint32_t)(K / 2) : 0u);
     // tile 0 = gate rows pcol + lrow, tile 1 = up rows n_out + pcol + lrow
-    uint32_t wvoff[2];
-    int lds_row[2];
+    uint32_t wvoff[TT];
+    int lds_row[TT];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TT; ++tt) {
         lds_row[tt] = tt * kGuCols + wave * 16 + lrow;
         wvoff[tt] = (uint32_t)((tt ? n_out : 0) + pcol + lrow) * (uint32_t)(K / 2) +
                     (uint32_t)(quarter * (G / 8));
     }
-    Frag<G> bq[P][2][SG];
+    Frag<G> bq[P][TT][SG];
     auto issue_w = [&](int st, int s) {           // step s into register stage st
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
             for (int h = 0; h < SG; ++h) {
                 const int gi = s * SG + h;
@@ -358,9 +364,9 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
         }
     }
 
-    f32x4 acc[2][NMS];
+    f32x4 acc[TT][NMS];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms)
             acc[tt][ms] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -387,33 +393,33 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
                 for (int h = 0; h < SG; ++h) {
                     const int gi = s * SG + h;
                     const int gc = min(gi, NG - 1);
-                    float scale[2];
-                    f16x2 c1024[2], c64[2];
+                    float scale[TT];
+                    f16x2 c1024[TT], c64[TT];
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
+                    for (int tt = 0; tt < TT; ++tt) {
                         zero_point_consts(lds_z[lds_row[tt] * NG + gc], c1024[tt], c64[tt]);
                         const float sc = (float)__builtin_bit_cast(_Float16, lds_s[lds_row[tt] * NG + gc]);
                         scale[tt] = gi < NG ? sc : 0.0f;
                     }
-                    f32x4 part[2][NMS];
+                    f32x4 part[TT][NMS];
 #pragma unroll
                     for (int t = 0; t < kWords; ++t) {
-                        f16x8 bop[2];
+                        f16x8 bop[TT];
 #pragma unroll
-                        for (int tt = 0; tt < 2; ++tt)
+                        for (int tt = 0; tt < TT; ++tt)
                             bop[tt] = dequant8(frag_word<G>(bq[st][tt][h], t), c1024[tt], c64[tt]);
                         const int seg = h * (G / 8) + quarter * (G / 32) + t;   // this lane's 8 K positions
 #pragma unroll
                         for (int ms = 0; ms < NMS; ++ms) {
                             const f16x8 aop = __builtin_bit_cast(f16x8, xb[(ms * 16 + lrow) * kStepPitch + seg]);
 #pragma unroll
-                            for (int tt = 0; tt < 2; ++tt)
+                            for (int tt = 0; tt < TT; ++tt)
                                 part[tt][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                     aop, bop[tt], t == 0 ? zero4 : part[tt][ms], 0, 0, 0);
                         }
                     }
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt)
+                    for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
                         for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
@@ -427,8 +433,9 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
     }
 
     // ---- 4. epilogue: H = gelu_tanh(gate) * up in fp16 at the tile's padded
-    // row, permuted per 8 columns. MFMA 16x16 output: lane holds rows
-    // 4 * quarter + i, column lrow.
+    // row, permuted per 8 columns (or, ungated, the fp16 output in natural
+    // column order). MFMA 16x16 output: lane holds rows 4 * quarter + i,
+    // column lrow.
     if (!live)
         return;
     uint16_t *H = static_cast<uint16_t *>(p.out);
@@ -440,8 +447,12 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
             const int r = ms * 16 + quarter * 4 + i;
             if (r >= valid)
                 continue;
-            const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
-            H[(size_t)(row0 + r) * n_out + permuted_col(col)] = __builtin_bit_cast(uint16_t, (_Float16)h);
+            if constexpr (GATED) {
+                const float h = gelu_tanh(acc[0][ms][i]) * acc[TT - 1][ms][i];
+                H[(size_t)(row0 + r) * n_out + permuted_col(col)] = __builtin_bit_cast(uint16_t, (_Float16)h);
+            } else {
+                H[(size_t)(row0 + r) * n_out + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[0][ms][i]);
+            }
         }
     }
 }
@@ -472,14 +483,51 @@ __attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
         return;
     if (p.K == kGuSteps * 256) {
         if (info.y > 16)
-            gate_up_body<G, 2, kGuSteps>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, kGuSteps, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, kGuSteps>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, kGuSteps, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
     } else {
         if (info.y > 16)
-            gate_up_body<G, 2, 0>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, 0, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, 0>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, 0, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+    }
+}
+
+// Dense W4A16 linear, y = x * deq(W)^T: the ungated body over the rows of x in
+// order (32-row tiles, the last one ragged), one weight matrix, no alignment.
+// Workgroup -> (column block, row tile), weight-sharing order: XCD x takes
+// column blocks x, x + 8, ... and runs all row tiles of a block back to back,
+// so the block's weights stream from HBM once and the other row tiles read
+// them from that XCD's L2 (x, at most a few MB, stays in every L2).
+template <int G>
+__global__ void __launch_bounds__(kGuThreads)
+__attribute__((amdgpu_waves_per_eu(3))) linear_kernel(GemmArgs p)
+{
+    const int nblocks = (p.n_out + kGuCols - 1) / kGuCols;
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int tile = slot % p.max_tiles;
+    const int cb = slot / p.max_tiles * kXcds + xcd;
+    if (cb >= nblocks)
+        return;
+    const int r0 = (int)threadIdx.x / kStepSeg;
+    int fidr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {                 // rows past the end read zeros
+        const int r = tile * kBlockM + r0 + i * (kGuThreads / kStepSeg);
+        fidr[i] = r < p.A ? r : p.A;
+    }
+    const int valid = min(kBlockM, p.A - tile * kBlockM);
+    if (p.K == kGuSteps * 256) {
+        if (valid > 16)
+            gate_up_body<G, 2, kGuSteps, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+        else
+            gate_up_body<G, 1, kGuSteps, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+    } else {
+        if (valid > 16)
+            gate_up_body<G, 2, 0, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+        else
+            gate_up_body<G, 1, 0, false>(p, 0, valid, tile * kBlockM, cb, fidr);
     }
 }
 
@@ -1356,6 +1404,25 @@ hipError_t launch_layer4(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
 }
 
 template <int G>
+hipError_t launch_linear_g(const GemmArgs &a, hipStream_t stream)
+{
+    const int nblocks = (a.n_out + kGuCols - 1) / kGuCols;
+    if (a.max_tiles == 0 || nblocks == 0)
+        return hipSuccess;
+    auto kern = linear_kernel<G>;
+    static size_t allowed = 64 * 1024;              // raised once per instantiation when needed
+    const size_t lds = gate_up_lds_bytes_k<G>(a.K);
+    hipError_t err = allow_lds(kern, lds, allowed);
+    if (err != hipSuccess)
+        return err;
+    const long long blocks = (long long)(nblocks + kXcds - 1) / kXcds * kXcds * a.max_tiles;
+    if (blocks > INT_MAX)
+        return hipErrorInvalidValue;
+    kern<<<dim3((unsigned)blocks), dim3(kGuThreads), lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int G>
 hipError_t launch_gate_up_g(const GemmArgs &a, hipStream_t stream)
 {
     const int nblocks = (a.n_out + kGuCols - 1) / kGuCols;
@@ -1416,6 +1483,11 @@ hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
     if (layer_shape_down(a, g))
         return launch_down4(a, stream);
     return g == 128 ? launch_down_g<128>(a, stream) : launch_down_g<64>(a, stream);
+}
+
+hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
+{
+    return g == 128 ? launch_linear_g<128>(a, stream) : launch_linear_g<64>(a, stream);
 }
 
 bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g)
