@@ -21,4 +21,7 @@ from .api import (  # noqa: F401
     moe_forward,
     gelu_tanh,
     threads,
+    philox4x32_10,
+    gumbel_score,
+    sample,
 )

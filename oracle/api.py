@@ -49,8 +49,12 @@ def load():
         lib.orc_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P]
         lib.orc_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                         P, P, P, I, P, P, P, I, P, I, P, P]
+        lib.orc_philox4x32_10.argtypes = [P, P, P]
+        lib.orc_gumbel_score.restype = ctypes.c_float
+        lib.orc_gumbel_score.argtypes = [ctypes.c_float, I, I, ctypes.c_uint64]
+        lib.orc_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P]
         for f in ("orc_quantize_rtn", "orc_dequant", "orc_align",
-                  "orc_w4a16_linear", "orc_moe_forward"):
+                  "orc_w4a16_linear", "orc_moe_forward", "orc_sample"):
             getattr(lib, f).restype = I
         _lib = lib
     return _lib
@@ -185,3 +189,32 @@ def moe_forward(x, ids, w, gu, dn, E: int, tokens=None, want_y: bool = False):
     if rc != 0:
         raise ValueError("orc_moe_forward: invalid arguments")
     return (out, y) if want_y else out
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    """Philox4x32-10 block: ctr 4 x uint32, key 2 x uint32 -> 4 x uint32."""
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.empty(4, np.uint32)
+    load().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def gumbel_score(l: float, r: int, v: int, seed: int) -> float:
+    return float(load().orc_gumbel_score(float(l), int(r), int(v), int(seed)))
+
+
+def sample(logits, seed: int):
+    """logits fp32 [R, V] -> (entropy fp64 [R], sample int32 [R], argmax int32 [R],
+    winning Gumbel score fp32 [R])."""
+    lg = _c(logits, np.float32)
+    R, V = lg.shape
+    h = np.empty(R, np.float64)
+    smp = np.empty(R, np.int32)
+    am = np.empty(R, np.int32)
+    sc = np.empty(R, np.float32)
+    rc = load().orc_sample(_p(lg), R, V, int(seed), _p(h), _p(smp), _p(am), _p(sc))
+    if rc != 0:
+        raise ValueError("orc_sample: invalid shape")
+    return h, smp, am, sc
+

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the W4A16 routed-expert layer.
+ * CPU oracle for the W4A16 routed-expert layer (and the sampler that follows
+ * it in a denoising step).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may load, link or
  * call this file: it is used by tests/, __graft_entry__.smoke() and the
@@ -424,3 +425,121 @@ int orc_moe_forward(const uint16_t *x, const int32_t *ids, const float *w,
     }
     return bad ? -1 : 0;
 }
+
+/* -------------------------------------------------------------- sampler ---- */
+
+/*
+ * The sampler of a denoising step ([kcard] "Sampler": fused_entropy computes
+ * Categorical(logits).entropy() in one streaming pass; gumbel_argmax_sample
+ * returns a Categorical sample by Gumbel-max, with Philox noise generated
+ * inline, and the plain argmax from the same pass).
+ *
+ * Philox4x32-10, written from its published definition (Salmon, Moraes,
+ * Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): a
+ * 4 x 32-bit counter c and a 2 x 32-bit key k; each of the 10 rounds forms
+ * the 64-bit products c0 * 0xD2511F53 and c2 * 0xCD9E8D57 and sets
+ *   c = { hi(c2 * 0xCD9E8D57) ^ c1 ^ k0, lo(c2 * 0xCD9E8D57),
+ *         hi(c0 * 0xD2511F53) ^ c3 ^ k1, lo(c0 * 0xD2511F53) },
+ * the key being advanced by the Weyl increments (0x9E3779B9, 0xBB67AE85)
+ * before every round but the first.
+ */
+void orc_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out)
+{
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n1 = (uint32_t)p1;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n3 = (uint32_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/*
+ * Gumbel score of logit l at (row r, column v) under `seed` (reading of the
+ * kernel card's "noise comes from Philox inline"; the pages do not fix the
+ * stream): the Philox block with counter {v / 4, r, 0, 0} and key
+ * {seed low 32 bits, seed high 32 bits}, its word v % 4 as w; the uniform
+ * U = (w / 256 + 1/2) / 2^24 in (0, 1), exact in fp32; the standard Gumbel
+ * variate G = -log(-log U); score = l + G. Everything after the integer step
+ * is fp32 (the precision the GPU kernel takes the decision in).
+ */
+float orc_gumbel_score(float l, int r, int v, uint64_t seed)
+{
+    const uint32_t ctr[4] = {(uint32_t)v >> 2, (uint32_t)r, 0u, 0u};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    const float u = ((float)(w[v & 3] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+    const float g = -logf(-logf(u));
+    return l + g;
+}
+
+/*
+ * For each of R rows of V fp32 logits:
+ *   entropy[r] = -sum_v p_v log p_v with p = softmax(row), in fp64
+ *                (log-sum-exp with the row maximum subtracted);
+ *   argmax[r]  = the first v with the largest logit;
+ *   sample[r]  = the first v with the largest orc_gumbel_score (a draw from
+ *                Categorical(softmax(row)): Gumbel-max);
+ *   score[r]   = that largest score (for checking near-ties).
+ * Any of the outputs may be NULL. Returns 0, or -1 on invalid arguments.
+ */
+int orc_sample(const float *logits, int R, int V, uint64_t seed, double *entropy,
+               int32_t *sample, int32_t *argmax, float *score)
+{
+    if (R < 0 || V <= 0 || !logits)
+        return -1;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < R; ++r) {
+        const float *row = logits + r * (long)V;
+        int am = 0;
+        for (int v = 1; v < V; ++v)
+            if (row[v] > row[am])
+                am = v;
+        if (argmax)
+            argmax[r] = am;
+        if (entropy) {
+            const double m = row[am];
+            double z = 0.0, s = 0.0;
+            for (int v = 0; v < V; ++v) {
+                const double d = (double)row[v] - m;
+                const double e = exp(d);
+                z += e;
+                s += e * d;
+            }
+            entropy[r] = log(z) - s / z;     /* -sum p (d - log z) */
+        }
+        if (sample || score) {
+            int best = 0;
+            float bs = orc_gumbel_score(row[0], (int)r, 0, seed);
+            for (int v = 1; v < V; ++v) {
+                const float sc = orc_gumbel_score(row[v], (int)r, v, seed);
+                if (sc > bs) {
+                    bs = sc;
+                    best = v;
+                }
+            }
+            if (sample)
+                sample[r] = best;
+            if (score)
+                score[r] = bs;
+        }
+    }
+    return 0;
+}
+
