@@ -199,6 +199,55 @@ def bench_linear(torch, dg, dev, args) -> int:
     return 0
 
 
+def bench_sampler(torch, dg, dev, args) -> int:
+    """The sampler of a denoising step on the pages' tensor: fp32 logits
+    [256, 262144] (268 MB, more than the Infinity Cache, rotated over 4
+    copies), one pass for entropy, Gumbel-max sample and argmax; also the
+    entropy-only pass. Prints one JSON line of its own."""
+    from synth import sampler_logits
+    R, V = 256, 262144
+    copies = [torch.from_numpy(sampler_logits(31 + c, R, V, 2.0)).to(dev) for c in range(4)]
+    n = R * V * 4
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(entropy: bool, draw: bool) -> float:
+        for i in range(8):
+            dg.sample(copies[i % 4], i, entropy=entropy, draw=draw, workspace=ws)
+        steps = max(20, args.steps // 30)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(steps):
+            dg.sample(copies[i % 4], i, entropy=entropy, draw=draw, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    ms_all = timed(True, True)
+    ms_ent = timed(True, False)
+    probe = read_probe(torch, dg, dev)
+    gbps = n / (ms_all * 1e-3) / 1e9
+    gbps_ent = n / (ms_ent * 1e-3) / 1e9
+    log(f"[sampler] entropy+sample+argmax {ms_all * 1e3:.1f} us ({gbps:.1f} GB/s); "
+        f"entropy+argmax {ms_ent * 1e3:.1f} us ({gbps_ent:.1f} GB/s); read probe {probe['gbps']} GB/s")
+    print(json.dumps({
+        "metric": "us per sampler pass (entropy + Gumbel-max sample + argmax) + achieved HBM GB/s",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": max(20, args.steps // 30),
+        "warmup": 8, "ms_per_step": round(ms_all, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"sampler: fp32 logits [{R}, {V}] ~ N(0, 2), 4 copies in rotation"},
+        "us_per_call": round(ms_all * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "entropy_only": {"us_per_call": round(ms_ent * 1e3, 2), "gbps": round(gbps_ent, 1),
+                         "pct_of_8TBps": round(100 * gbps_ent / HBM_PEAK_GBPS, 2)},
+        "hbm_probe": probe,
+        "roofline": {"kernel": "sample_partial_kernel<true>", "bound": "hbm", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def cpu_baseline(shape):
     """The CPU oracle, as it stands, on one full layer drawn on the host."""
     import oracle
@@ -230,8 +279,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=3000, help="timed layer forwards")
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--layers", type=int, default=30, help="distinct weight sets in rotation")
-    ap.add_argument("--workload", default="stack", choices=["stack", "full", "skew", "wide", "lmhead"],
-                    help="lmhead: the dense W4A16 linear at T=256, K=2816, N=262144 (not the layer)")
+    ap.add_argument("--workload", default="stack", choices=["stack", "full", "skew", "wide", "lmhead", "sampler"],
+                    help="lmhead: the dense W4A16 linear at T=256, K=2816, N=262144; sampler: "
+                         "entropy + Gumbel-max sample + argmax over [256, 262144] fp32 logits "
+                         "(neither is the layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 5 times (the counter "
@@ -264,6 +315,8 @@ def main() -> int:
         return 0
     if args.workload == "lmhead":
         return bench_linear(torch, dg, dev, args)
+    if args.workload == "sampler":
+        return bench_sampler(torch, dg, dev, args)
     shape = CONFIGS[args.workload]
     L = args.layers if args.workload == "stack" else 1
     if args.workload != "stack":

@@ -209,6 +209,33 @@ DGW4_API int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uin
                                void *stream);
 
 /*
+ * dgw4_sample — the sampler of a denoising step, in one streaming pass over
+ * R rows of V fp32 logits ([kcard] "Sampler": fused_entropy and
+ * gumbel_argmax_sample; here one pass gives both):
+ *   entropy[r] = -sum_v p_v log p_v, p = softmax(row r), fp32 nats;
+ *   argmax[r]  = the first v with the largest logit;
+ *   sample[r]  = the first v with the largest l_v + G_v, a draw from
+ *                Categorical(p) by Gumbel-max. G_v = -log(-log U_v) in fp32;
+ *                U_v = (w / 256 + 1/2) / 2^24 with w word v % 4 of the
+ *                Philox4x32-10 block with counter {v / 4, r, 0, 0} and key
+ *                {seed & 0xffffffff, seed >> 32}. Same seed, same draw.
+ * logits: device, row-major [R, V], 16-byte aligned, finite or -inf (masked,
+ * probability 0), at least one finite value per row. entropy (fp32 [R]),
+ * sample and argmax (int32 [R]): device, each may be NULL to skip it (NULL
+ * sample also skips the noise). CUB-style workspace: workspace == NULL
+ * writes the size to *ws_bytes and returns DGW4_OK; otherwise at least that
+ * many bytes, 16-byte aligned, caller-owned. Every reduction has a fixed
+ * order: results are bitwise reproducible.
+ * Returns DGW4_ERR_INVALID_ARG (null ws_bytes, R < 0, V < 4, misaligned or
+ * null pointers), DGW4_ERR_UNSUPPORTED (V not a multiple of 4, R * V >=
+ * 2^40), DGW4_ERR_WORKSPACE (*ws_bytes too small), DGW4_ERR_HIP.
+ * Enqueued on `stream`; no host synchronisation.
+ */
+DGW4_API int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float *entropy,
+                         int32_t *sample, int32_t *argmax, void *workspace, size_t *ws_bytes,
+                         void *stream);
+
+/*
  * dgw4_hbm_read_probe — a measurement aid, not a step of the layer: reads
  * `bytes` bytes of device memory at `buf` once, with the whole chip
  * (16-byte non-temporal loads, several in flight per lane), so that the elapsed time on

@@ -497,7 +497,9 @@ float orc_gumbel_score(float l, int r, int v, uint64_t seed)
  *   sample[r]  = the first v with the largest orc_gumbel_score (a draw from
  *                Categorical(softmax(row)): Gumbel-max);
  *   score[r]   = that largest score (for checking near-ties).
- * Any of the outputs may be NULL. Returns 0, or -1 on invalid arguments.
+ * Logits are finite or -inf (a masked entry, probability 0); a row needs one
+ * finite logit. Any of the outputs may be NULL. Returns 0, or -1 on invalid
+ * arguments.
  */
 int orc_sample(const float *logits, int R, int V, uint64_t seed, double *entropy,
                int32_t *sample, int32_t *argmax, float *score)
@@ -520,7 +522,8 @@ int orc_sample(const float *logits, int R, int V, uint64_t seed, double *entropy
                 const double d = (double)row[v] - m;
                 const double e = exp(d);
                 z += e;
-                s += e * d;
+                if (e > 0.0)                 /* a -inf logit adds p log p = 0 */
+                    s += e * d;
             }
             entropy[r] = log(z) - s / z;     /* -sum p (d - log z) */
         }

@@ -15,4 +15,5 @@ from .inputs import (  # noqa: F401
     routing,
     zipf_prior,
     linear_inputs,
+    sampler_logits,
 )

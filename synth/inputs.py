@@ -151,3 +151,9 @@ def linear_inputs(seed: int, T: int, K: int, N: int, std: float = 0.02,
     x = _normal_rows(seed * 2 + 1, T, K, 1.0, threads).astype(np.float16)
     w = _normal_rows(seed * 2, N, K, std, threads)
     return x, w
+
+
+def sampler_logits(seed: int, R: int, V: int, std: float = 2.0, threads: int = 8) -> np.ndarray:
+    """fp32 logits [R, V] ~ N(0, std), one child stream per row."""
+    return _normal_rows(seed, R, V, std, threads)
+

@@ -123,3 +123,20 @@ def test_linear_rejects():
     assert f(p + 8, 4, 256, 64, p, p, p, 64, p, None) == B.ERR_INVALID_ARG   # alignment
     assert f(None, 0, 256, 64, None, None, None, 64, None, None) == B.OK     # T = 0: no-op
 
+
+def test_sample_workspace_and_rejects():
+    import ctypes
+    f = dg.lib().dgw4_sample
+    n = ctypes.c_size_t(0)
+    assert f(None, 256, 262144, 1, None, None, None, None, ctypes.byref(n), None) == B.OK
+    assert n.value == 256 * 8 * 32                       # 8 splits per row, 32-byte partials
+    assert f(None, 256, 262146, 1, None, None, None, None, ctypes.byref(n), None) == B.ERR_UNSUPPORTED
+    assert f(None, -1, 1024, 1, None, None, None, None, ctypes.byref(n), None) == B.ERR_INVALID_ARG
+    assert f(None, 4, 1024, 1, None, None, None, None, None, None) == B.ERR_INVALID_ARG
+    p = 1 << 12
+    small = ctypes.c_size_t(8)
+    assert f(p, 4, 1024, 1, None, None, None, p, ctypes.byref(small), None) == B.ERR_WORKSPACE
+    big = ctypes.c_size_t(1 << 20)
+    assert f(p + 4, 4, 1024, 1, None, None, None, p, ctypes.byref(big), None) == B.ERR_INVALID_ARG
+    assert f(None, 0, 1024, 1, None, None, None, p, ctypes.byref(big), None) == B.OK   # R = 0
+

@@ -17,4 +17,7 @@ from .binding import (  # noqa: F401
     version,
     workspace_bytes,
     w4a16_linear,
+    sample,
+    fused_entropy,
+    gumbel_argmax_sample,
 )

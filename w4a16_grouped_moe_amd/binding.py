@@ -65,6 +65,8 @@ def lib():
                                              ctypes.POINTER(P), I]
         L.dgw4_w4a16_linear.restype = I
         L.dgw4_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P, P]
+        L.dgw4_sample.restype = I
+        L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
         L.dgw4_hbm_read_probe.restype = I
         L.dgw4_hbm_read_probe.argtypes = [P, S, P, P]
         _lib = L
@@ -146,6 +148,45 @@ def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> 
     py = _dev(out, "out", _F16)
     _check("dgw4_w4a16_linear", lib().dgw4_w4a16_linear(px, T, K, N, pq, ps, pz, g, py, _stream(x)))
     return out
+
+
+def sample(logits: torch.Tensor, seed: int = 0, entropy: bool = True, draw: bool = True,
+           workspace: torch.Tensor | None = None):
+    """The sampler in one pass over fp32 logits [R, V] (V a multiple of 4):
+    returns (entropy fp32 [R] or None, sample int32 [R] or None, argmax int32 [R]).
+    The sample is a Gumbel-max draw from Categorical(softmax(row)) with
+    Philox4x32-10 noise keyed by ``seed`` (see dgw4_sample)."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    pl = _dev(logits, "logits", (torch.float32,))
+    n = ctypes.c_size_t(0)
+    _check("dgw4_sample", lib().dgw4_sample(None, R, V, int(seed) & (2**64 - 1), None, None, None,
+                                            None, ctypes.byref(n), None))
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 16), dtype=torch.uint8, device=logits.device)
+    pws = _dev(workspace, "workspace", (torch.uint8,))
+    n = ctypes.c_size_t(workspace.numel())
+    dev = logits.device
+    h = torch.empty(R, dtype=torch.float32, device=dev) if entropy else None
+    smp = torch.empty(R, dtype=torch.int32, device=dev) if draw else None
+    am = torch.empty(R, dtype=torch.int32, device=dev)
+    _check("dgw4_sample", lib().dgw4_sample(
+        pl, R, V, int(seed) & (2**64 - 1), h.data_ptr() if h is not None else None,
+        smp.data_ptr() if smp is not None else None, am.data_ptr(), pws, ctypes.byref(n),
+        _stream(logits)))
+    return h, smp, am
+
+
+def fused_entropy(logits: torch.Tensor) -> torch.Tensor:
+    """Categorical(logits).entropy() in nats, one pass (no noise drawn)."""
+    return sample(logits, 0, entropy=True, draw=False)[0]
+
+
+def gumbel_argmax_sample(logits: torch.Tensor, seed: int):
+    """(Gumbel-max sample, argmax) of each row, one pass."""
+    _, smp, am = sample(logits, seed, entropy=False, draw=True)
+    return smp, am
 
 
 def align_capacity(T: int, topk: int, E: int, block_m: int) -> int:

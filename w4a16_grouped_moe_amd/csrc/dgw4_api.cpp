@@ -303,4 +303,27 @@ int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
     return from_hip(dgw4::launch_linear(a, g, (hipStream_t)stream));
 }
 
+int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float *entropy, int32_t *sample,
+                int32_t *argmax, void *workspace, size_t *ws_bytes, void *stream)
+{
+    if (!ws_bytes || R < 0 || V < 4)
+        return DGW4_ERR_INVALID_ARG;
+    if (V % 4 != 0 || (long long)R * V >= (1LL << 40) || V >= (1 << 30))
+        return DGW4_ERR_UNSUPPORTED;
+    const size_t need = dgw4::sample_workspace_bytes(R, V);
+    if (!workspace) {
+        *ws_bytes = need;
+        return DGW4_OK;
+    }
+    if (*ws_bytes < need)
+        return DGW4_ERR_WORKSPACE;
+    if (R == 0)
+        return DGW4_OK;
+    if (!logits || !aligned(logits, 16) || !aligned(workspace, 16))
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_sample(logits, R, V, seed, entropy, sample, argmax, workspace,
+                                        (hipStream_t)stream));
+}
+
 }  // extern "C"
+

@@ -69,6 +69,14 @@ bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn
 hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
                                hipStream_t stream);
 
+// Sampler: splits per row, workspace bytes, and the two launches (partials,
+// then the per-row merge). V is a multiple of 4; any output may be null
+// (sample == null skips the noise).
+int sample_splits(int R, int V);
+size_t sample_workspace_bytes(int R, int V);
+hipError_t launch_sample(const float *logits, int R, int V, uint64_t seed, float *entropy,
+                         int32_t *sample, int32_t *argmax, void *workspace, hipStream_t stream);
+
 // One read of `bytes` (a multiple of 16) at buf over the whole chip; see
 // dgw4_hbm_read_probe.
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
