@@ -189,6 +189,20 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     void *stream, void *const *events, int n_events);
 
 /*
+ * dgw4_forward_timeouts — a diagnostic for dgw4_moe_forward at the layer's
+ * shape, where gate_up and down run as one launch and each workgroup waits,
+ * with a bounded number of polls, for the other half of its tile's H. Writes
+ * to *timeouts (host memory) how many such waits of the last forward on
+ * `workspace` reached the bound (0 for every correct launch; a nonzero count
+ * means that forward's output is not to be trusted). T, topk, E, d, m: as
+ * passed to that forward. Unlike the other calls this one synchronises
+ * `stream` (it copies one word to the host). DGW4_ERR_INVALID_ARG for null
+ * pointers or invalid sizes, DGW4_ERR_HIP if the copy fails.
+ */
+DGW4_API int dgw4_forward_timeouts(const void *workspace, int T, int topk, int E, int d, int m,
+                                   int32_t *timeouts, void *stream);
+
+/*
  * dgw4_w4a16_linear — the dense W4A16 linear layer: y = x * deq(W)^T
  * ([kcard] "W4A16": w4a16_linear(x, qw, scale, zero) equals F.linear(x,
  * dequant(W)); the same packing and the same GEMM core as the routed-expert

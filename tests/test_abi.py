@@ -140,3 +140,13 @@ def test_sample_workspace_and_rejects():
     assert f(p + 4, 4, 1024, 1, None, None, None, p, ctypes.byref(big), None) == B.ERR_INVALID_ARG
     assert f(None, 0, 1024, 1, None, None, None, p, ctypes.byref(big), None) == B.OK   # R = 0
 
+
+def test_forward_timeouts_rejects():
+    import ctypes
+    f = dg.lib().dgw4_forward_timeouts
+    out = ctypes.c_int32(0)
+    p = 1 << 12
+    assert f(None, 256, 8, 128, 2816, 704, ctypes.byref(out), None) == B.ERR_INVALID_ARG
+    assert f(p, 256, 8, 128, 2816, 704, None, None) == B.ERR_INVALID_ARG
+    assert f(p, -1, 8, 128, 2816, 704, ctypes.byref(out), None) == B.ERR_INVALID_ARG
+

@@ -179,6 +179,8 @@ def test_forward_full_deterministic_100(full_layer):
     torch.cuda.synchronize()
     lc.log(f"[determinism] 100 runs, {bad} differing")
     assert bad == 0
+    sh = L.shape
+    assert dg.forward_timeouts(ws, sh.T, sh.topk, sh.E, sh.d, sh.m) == 0
 
 
 def test_forward_layer_shape_unfused_sampled():

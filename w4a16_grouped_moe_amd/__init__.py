@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     w4a16_linear,
     sample,
     fused_entropy,
+    forward_timeouts,
     gumbel_argmax_sample,
 )

@@ -65,6 +65,8 @@ def lib():
                                              ctypes.POINTER(P), I]
         L.dgw4_w4a16_linear.restype = I
         L.dgw4_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P, P]
+        L.dgw4_forward_timeouts.restype = I
+        L.dgw4_forward_timeouts.argtypes = [P, I, I, I, I, I, P, P]
         L.dgw4_sample.restype = I
         L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
         L.dgw4_hbm_read_probe.restype = I
@@ -125,6 +127,16 @@ def quantize_rtn(w: torch.Tensor, g: int):
     _check("dgw4_quantize_rtn", lib().dgw4_quantize_rtn(
         pw, E, N, K, g, q.data_ptr(), s.data_ptr(), z.data_ptr(), _stream(w)))
     return q, s, z
+
+
+def forward_timeouts(workspace: torch.Tensor, T: int, topk: int, E: int, d: int, m: int) -> int:
+    """How many bounded partner waits of the last moe_forward on ``workspace``
+    gave up (0 for every correct launch). Synchronises the current stream."""
+    pws = _dev(workspace, "workspace", (torch.uint8,))
+    out = ctypes.c_int32(-1)
+    _check("dgw4_forward_timeouts", lib().dgw4_forward_timeouts(
+        pws, T, topk, E, d, m, ctypes.byref(out), _stream(workspace)))
+    return int(out.value)
 
 
 def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> torch.Tensor:

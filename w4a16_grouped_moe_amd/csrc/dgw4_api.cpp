@@ -51,7 +51,7 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
-    L.ready = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
+    L.ready = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM + 1));   // + the timeout count
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take(sizeof(uint16_t) * (size_t)A * (size_t)d);
@@ -195,7 +195,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     if (err == hipSuccess)
         err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
                                  offsets, sorted_ids, tile_expert, num_padded, tile_info, ready,
-                                 (int)(cap / dgw4::kBlockM), st);
+                                 (int)(cap / dgw4::kBlockM) + 1, st);
     if (err == hipSuccess)
         err = mark(1);
     if (err != hipSuccess)
@@ -323,6 +323,24 @@ int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float *entropy
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_sample(logits, R, V, seed, entropy, sample, argmax, workspace,
                                         (hipStream_t)stream));
+}
+
+int dgw4_forward_timeouts(const void *workspace, int T, int topk, int E, int d, int m,
+                          int32_t *timeouts, void *stream)
+{
+    if (!workspace || !timeouts || T < 0 || topk < 1 || E < 1 || d < 1 || m < 1)
+        return DGW4_ERR_INVALID_ARG;
+    const size_t cap = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
+    if (cap == 0)
+        return DGW4_ERR_INVALID_ARG;
+    const Layout L = layout((long long)T * topk, T, E, d, m, (long long)cap);
+    const char *slot = static_cast<const char *>(workspace) + L.ready +
+                       sizeof(int32_t) * (cap / dgw4::kBlockM);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t err = hipMemcpyAsync(timeouts, slot, sizeof(int32_t), hipMemcpyDeviceToHost, st);
+    if (err == hipSuccess)
+        err = hipStreamSynchronize(st);
+    return from_hip(err);
 }
 
 }  // extern "C"

@@ -64,7 +64,8 @@ hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
 
 // Whether the pair of GEMMs runs as one launch (the layer's shape), and that
-// launch: ready holds one zeroed counter per tile (gu.max_tiles of them).
+// launch: ready holds one zeroed counter per tile (gu.max_tiles of them) and
+// one more, ready[gu.max_tiles], that counts partner waits which gave up.
 bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g);
 hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
                                hipStream_t stream);

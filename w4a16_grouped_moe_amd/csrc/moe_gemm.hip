@@ -852,14 +852,17 @@ constexpr int kSpinLimit = 1 << 16;
 
 // One lane waits until *flag >= target (device-scope loads); the rest of the
 // workgroup follows through a barrier, and the data the counter announces is
-// then read with device-scope loads.
-__device__ __noinline__ void wait_count(const int32_t *flag, int target)
+// then read with device-scope loads. A wait that reaches the bound (which a
+// correct launch never does) is counted in *timeouts, so that a caller can
+// tell that the outputs of that call are not to be trusted.
+__device__ __noinline__ void wait_count(const int32_t *flag, int target, int32_t *timeouts)
 {
     for (int i = 0; i < kSpinLimit; ++i) {
         if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target)
-            break;
+            return;
         __builtin_amdgcn_s_sleep(2);
     }
+    __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kL4Waves = 11;
@@ -1121,7 +1124,8 @@ constexpr int vmcnt_at_most(int n)
 // both halves.
 template <int NMS, bool FUSED>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
-                                           uint4 (&av)[kDn4ALoads], int fid, int32_t *ready)
+                                           uint4 (&av)[kDn4ALoads], int fid, int32_t *ready,
+                                           int32_t *ready_end)
 {
     constexpr int G = 64;
     constexpr int P = kDn4Ahead;
@@ -1183,7 +1187,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
         __syncthreads();                           // also: every wave is done with gate_up's LDS
         if (tid == 0) {
             __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_count(ready, 2);
+            wait_count(ready, 2, ready_end);
         }
     }
 
@@ -1308,9 +1312,9 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     if (info.x < 0)
         return;
     if (info.y > 16)
-        down4_body<2, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr);
+        down4_body<2, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
     else
-        down4_body<1, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr);
+        down4_body<1, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
 }
 
 // ---- gate_up and down of the layer's shape in one launch. Workgroup (tile,
@@ -1319,7 +1323,8 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
 // are there. The two halves of a tile are neighbours in dispatch order on
 // one XCD, so a workgroup only ever waits for a partner that is resident or
 // next in line, and H stays in that XCD's L2. The counters start at zero
-// (the alignment step clears them) and the wait is bounded.
+// (the alignment step clears them) and the wait is bounded; ready[max_tiles]
+// counts waits that hit the bound.
 constexpr size_t layer4_lds_bytes()
 {
     return gate_up4_lds_bytes() > down4_lds_bytes() ? gate_up4_lds_bytes() : down4_lds_bytes();
@@ -1353,9 +1358,9 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
     __builtin_amdgcn_sched_barrier(0);
     uint4 av[kDn4ALoads];
     if (info.y > 16)
-        down4_body<2, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile);
+        down4_body<2, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
     else
-        down4_body<1, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile);
+        down4_body<1, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
 }
 
 template <class Kern>
