@@ -130,6 +130,31 @@ def test_forward_shapes_every_element(case):
     lc.assert_close(lc.gpu_forward(L), lc.oracle_forward(L), case["name"])
 
 
+@pytest.mark.parametrize("T", [1, 5, 37])
+def test_forward_layer_shape_small_T_every_element(T):
+    # the one-launch gate_up + down path with nearly empty, ragged tiles
+    shp = lc.custom_shape(f"fused_T{T}", E=16, topk=8, T=T, d=2816, m=704, index=92)
+    L = lc.build(shp)
+    lc.assert_close(lc.gpu_forward(L), lc.oracle_forward(L), f"layer shape T={T}")
+
+
+def test_forward_layer_shape_duplicate_and_dropped_ids():
+    shp = lc.custom_shape("fused_dups", E=16, topk=8, T=24, d=2816, m=704, index=93)
+    rng = np.random.default_rng(8)
+    ids = rng.integers(0, 16, (24, 8)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]                                   # duplicates are independent
+    w = rng.uniform(0.1, 1, (24, 8)).astype(np.float32)
+    bad = ids.copy()
+    bad[::3, 2] = -1                                        # dropped by the GPU path
+    bad[1::5, 7] = 16
+    L = lc.build(shp, ids=bad, w=w)
+    gpu = lc.gpu_forward(L)
+    keep = (bad >= 0) & (bad < 16)
+    L.ids = np.where(keep, bad, 0).astype(np.int32)
+    L.w = np.where(keep, w, 0).astype(np.float32)
+    lc.assert_close(gpu, lc.oracle_forward(L), "layer shape dups/dropped")
+
+
 def test_forward_duplicate_and_dropped_ids():
     shp = lc.custom_shape("dups", E=8, topk=4, T=40, d=512, m=192)
     rng = np.random.default_rng(3)
