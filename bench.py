@@ -283,6 +283,9 @@ def main() -> int:
                     help="lmhead: the dense W4A16 linear at T=256, K=2816, N=262144; sampler: "
                          "entropy + Gumbel-max sample + argmax over [256, 262144] fp32 logits "
                          "(neither is the layer)")
+    ap.add_argument("--weight-layout", default="tiled", choices=["tiled", "canonical"],
+                    help="layout of the packed weights the timed steps read (both give "
+                         "identical results; the other one is timed in a short pass too)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 5 times (the counter "
@@ -326,15 +329,21 @@ def main() -> int:
     layers = []
     for l in range(L):
         gw, dw = expert_weights_device(shape, l, dev)
-        gu = (*dg.quantize_rtn(gw, shape.g_gu), shape.g_gu)
+        gu_c = (*dg.quantize_rtn(gw, shape.g_gu), shape.g_gu)
         del gw
-        dn = (*dg.quantize_rtn(dw, shape.g_dn), shape.g_dn)
+        dn_c = (*dg.quantize_rtn(dw, shape.g_dn), shape.g_dn)
         del dw
+        # the tiled copies: the same bytes in the GEMMs' load order (a
+        # load-time conversion, outside every timed region)
+        gu_t, dn_t = dg.pack_tiled(gu_c), dg.pack_tiled(dn_c)
+        tiled = args.weight_layout == "tiled"
         x = activations(shape, l)
         ids, w = routing(shape, l)
         populated = int(np.unique(ids).size)
         layers.append(dict(
-            gu=gu, dn=dn, x=torch.from_numpy(x).to(dev), ids=torch.from_numpy(ids).to(dev),
+            gu=gu_t if tiled else gu_c, dn=dn_t if tiled else dn_c,
+            gu_other=gu_c if tiled else gu_t, dn_other=dn_c if tiled else dn_t,
+            x=torch.from_numpy(x).to(dev), ids=torch.from_numpy(ids).to(dev),
             w=torch.from_numpy(w).to(dev), bytes=layer_bytes(shape, populated),
             populated=populated))
     torch.cuda.synchronize()
@@ -346,9 +355,10 @@ def main() -> int:
     out = torch.empty((shape.T, shape.d), dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, events=None):
+    def step(i, events=None, other=False):
         ly = layers[i % L]
-        dg.moe_forward(ly["x"], ly["ids"], ly["w"], ly["gu"], ly["dn"], workspace=ws, out=out,
+        gu, dn = (ly["gu_other"], ly["dn_other"]) if other else (ly["gu"], ly["dn"])
+        dg.moe_forward(ly["x"], ly["ids"], ly["w"], gu, dn, workspace=ws, out=out,
                        events=events)
 
     for i in range(args.warmup):
@@ -380,6 +390,19 @@ def main() -> int:
               "median_us_per_layer": round(float(np.median(sweep_us)), 2),
               "p10_us_per_layer": round(float(np.percentile(sweep_us, 10)), 2),
               "p90_us_per_layer": round(float(np.percentile(sweep_us, 90)), 2)}
+
+    # The same sweeps on the other weight layout (same results, other load
+    # addresses), for comparison.
+    torch.cuda.synchronize()
+    sw[0].record(stream)
+    for r in range(R):
+        for i in range(L):
+            step(i, other=True)
+        sw[r + 1].record(stream)
+    torch.cuda.synchronize()
+    other_us = np.array([sw[r].elapsed_time(sw[r + 1]) * 1e3 / L for r in range(R)])
+    other_layout = "canonical" if args.weight_layout == "tiled" else "tiled"
+    spread[f"{other_layout}_layout_median_us_per_layer"] = round(float(np.median(other_us)), 2)
 
     # The same sweep replayed as one HIP graph (captured once; every replay
     # re-runs alignment and both GEMMs on the device), checked bitwise
@@ -444,6 +467,7 @@ def main() -> int:
             "topk": shape.topk,
             "d": shape.d,
             "m": shape.m,
+            "weight_layout": args.weight_layout,
         },
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -453,7 +477,9 @@ def main() -> int:
         "graph_replay": graph,
         "hbm_probe": probe,
         "roofline": {
-            "kernel": "layer4_kernel (gate_up + GELU(tanh) gate + down in one launch, layer shape)",
+            "kernel": (f"layer4_kernel<{str(args.weight_layout == 'tiled').lower()}> (gate_up + "
+                       f"GELU(tanh) gate + down in one launch, layer shape, "
+                       f"{args.weight_layout} weights)"),
             "bound": "hbm",
             "achieved": round(gemm_gbps, 1),
             "peak": HBM_PEAK_GBPS,

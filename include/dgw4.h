@@ -32,6 +32,17 @@
  * An expert stack adds a leading [E] dimension to each of the three.
  * gate_up_proj of expert e is [2m, d]: rows 0..m-1 are the gate projection,
  * rows m..2m-1 the up projection. down_proj is [d, m].
+ *
+ * Tiled weight layout (this library's own, for gfx950; not a checkpoint
+ * format): the same bytes of q reordered so that the MFMA lanes' loads of one
+ * group of 16 rows are contiguous. With N % 16 == 0 and K % g == 0,
+ *   qt [N/16][K/g][4][16][g/8]   (an expert stack: [E] in front)
+ * where qt[b][j][p][r][i] = q[16 b + r][j g/2 + p g/8 + i]: block b of 16
+ * rows, group j, quarter p of the group's g/2 bytes, row r within the block.
+ * s and z keep their layout. dgw4_pack_tiled converts; the GEMM entry points
+ * take a matrix in that layout when its group-size argument carries
+ * DGW4_WEIGHTS_TILED (g | DGW4_WEIGHTS_TILED). Results are bit-identical to
+ * those of the canonical layout.
  */
 #ifndef DGW4_H
 #define DGW4_H
@@ -56,6 +67,9 @@ typedef enum {
     DGW4_ERR_WORKSPACE = 3,     /* workspace smaller than the queried size */
     DGW4_ERR_HIP = 4            /* a kernel launch failed */
 } dgw4_status;
+
+/* Or-ed into a GEMM's group-size argument: that matrix is in the tiled layout. */
+#define DGW4_WEIGHTS_TILED 0x10000
 
 /* Human-readable name of a status code (static storage). */
 DGW4_API const char *dgw4_status_string(int status);
@@ -89,6 +103,20 @@ DGW4_API const char *dgw4_last_error(void);
  */
 DGW4_API int dgw4_quantize_rtn(const float *w, int E, int N, int K, int g,
                       uint8_t *q, uint16_t *s, uint16_t *z, void *stream);
+
+/*
+ * dgw4_pack_tiled — reorder packed weights from the canonical layout into the
+ * tiled layout above (a pure byte permutation, bit-exact).
+ *   q       device uint8 [E, N, K/2], canonical, 8-byte aligned
+ *   E, N, K E >= 0, N % 16 == 0, K % g == 0
+ *   g       64 or 128 (others: DGW4_ERR_UNSUPPORTED), the group size the
+ *           matrix was quantised with
+ *   qt      device uint8 [E, N, K/2] (output), 8-byte aligned; must not
+ *           overlap q (DGW4_ERR_INVALID_ARG)
+ * E == 0 is a no-op. Enqueued on `stream`, no host sync.
+ */
+DGW4_API int dgw4_pack_tiled(const uint8_t *q, int E, int N, int K, int g, uint8_t *qt,
+                             void *stream);
 
 /*
  * dgw4_align_capacity — size of the padded assignment list for dgw4_align:
@@ -153,7 +181,10 @@ DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int blo
  *   gu_q/s/z   device, gate_up stack [E, 2m, d] packed with group gu_g
  *   dn_q/s/z   device, down stack [E, d, m] packed with group dn_g
  *              (x, the six pack pointers: 16-byte aligned; out: 8-byte aligned)
- *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED)
+ *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED), each or-ed
+ *              with DGW4_WEIGHTS_TILED when that stack's q is in the tiled
+ *              layout (same results; the layer's shape runs fastest with both
+ *              tiled). Other bits: DGW4_ERR_INVALID_ARG.
  *   workspace  device scratch of at least *ws_bytes bytes, 256-byte aligned.
  *              If workspace is NULL, the required size is written to
  *              *ws_bytes and nothing is launched. Contents on entry are
@@ -213,10 +244,12 @@ DGW4_API int dgw4_forward_timeouts(const void *workspace, int T, int topk, int E
  *   y  fp16 [T, N] row-major (written, caller-owned).
  * Each output is the fp32 sum over K of x times (q - z) with the group's
  * scale applied once per group in fp32, rounded once to fp16.
+ * g may carry DGW4_WEIGHTS_TILED (q in the tiled layout; same results).
  * Returns DGW4_ERR_INVALID_ARG for null pointers (T > 0), negative T, odd K,
- * K % g != 0 or misaligned pointers; DGW4_ERR_UNSUPPORTED for g not in
- * {64, 128}, N not a multiple of 16, more than 64 groups per row, or tensors
- * past 2 GiB. T == 0 is a no-op. Enqueued on `stream`, no host sync.
+ * K % g != 0, unknown flag bits in g or misaligned pointers;
+ * DGW4_ERR_UNSUPPORTED for g not in {64, 128}, N not a multiple of 16, more
+ * than 64 groups per row, or tensors past 2 GiB. T == 0 is a no-op. Enqueued
+ * on `stream`, no host sync.
  */
 DGW4_API int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
                                const uint16_t *s, const uint16_t *z, int g, uint16_t *y,

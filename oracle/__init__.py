@@ -4,7 +4,8 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package. The product path (the HIP library and
 its Python binding) never imports, links or calls it, and this package never
 imports the product path. The arithmetic lives in ``oracle.c`` (plain C, fp64
-forward, fp32 quantiser decisions); this module only marshals numpy arrays.
+forward, fp32 quantiser decisions); this module only marshals numpy arrays,
+except for ``pack_tiled``, a byte reordering written as a numpy transposition.
 Functions with no independent pin are marked "parity unpinned" in oracle.c's
 header and in the design doc (the gate/up row order and the choice of GELU(tanh)
 as the activation).
@@ -17,6 +18,7 @@ from .api import (  # noqa: F401
     quantize_rtn,
     dequant,
     align,
+    pack_tiled,
     w4a16_linear,
     moe_forward,
     gelu_tanh,

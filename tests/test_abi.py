@@ -150,3 +150,33 @@ def test_forward_timeouts_rejects():
     assert f(p, 256, 8, 128, 2816, 704, None, None) == B.ERR_INVALID_ARG
     assert f(p, -1, 8, 128, 2816, 704, ctypes.byref(out), None) == B.ERR_INVALID_ARG
 
+
+
+def test_pack_tiled_rejects():
+    f = dg.lib().dgw4_pack_tiled
+    p = 1 << 20
+    assert f(p, 1, 16, 128, 32, p + (1 << 16), None) == B.ERR_UNSUPPORTED        # g
+    assert f(p, 1, 24, 128, 64, p + (1 << 16), None) == B.ERR_INVALID_ARG        # N % 16
+    assert f(p, 1, 16, 96, 64, p + (1 << 16), None) == B.ERR_INVALID_ARG         # K % g
+    assert f(None, 1, 16, 128, 64, p, None) == B.ERR_INVALID_ARG
+    assert f(p, 1, 16, 128, 64, None, None) == B.ERR_INVALID_ARG
+    assert f(p + 4, 1, 16, 128, 64, p + (1 << 16), None) == B.ERR_INVALID_ARG    # alignment
+    assert f(p, 1, 16, 128, 64, p + 512, None) == B.ERR_INVALID_ARG              # overlap (1 KiB)
+    assert f(p, -1, 16, 128, 64, p + (1 << 16), None) == B.ERR_INVALID_ARG
+    assert f(None, 0, 16, 128, 64, None, None) == B.OK                           # E = 0: no-op
+
+
+def test_layout_flag_bits():
+    tiled = B.WEIGHTS_TILED
+    assert tiled == 0x10000
+    # the flag is accepted on either stack; any other high bit is not
+    assert _fwd(T=0, x=None, ids=None, w=None, out=None, gg=128 | tiled, dg=64 | tiled) == B.OK
+    assert _fwd(gg=128 | 0x20000) == B.ERR_INVALID_ARG
+    assert _fwd(dg=64 | (1 << 30)) == B.ERR_INVALID_ARG
+    assert _fwd(gg=-128) == B.ERR_INVALID_ARG
+    n = dg.workspace_bytes(256, 8, 128, 2816, 704, 128 | tiled, 64 | tiled)
+    assert n == dg.workspace_bytes(256, 8, 128, 2816, 704)
+    f = dg.lib().dgw4_w4a16_linear
+    p = 1 << 12
+    assert f(p, 4, 256, 64, p, p, p, 64 | 0x40000, p, None) == B.ERR_INVALID_ARG
+    assert f(None, 0, 256, 64, None, None, None, 64 | tiled, None, None) == B.OK

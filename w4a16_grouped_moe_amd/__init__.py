@@ -12,6 +12,8 @@ from .binding import (  # noqa: F401
     header_functions,
     lib,
     moe_forward,
+    pack_tiled,
+    WEIGHTS_TILED,
     quantize_rtn,
     status_string,
     version,

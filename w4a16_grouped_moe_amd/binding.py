@@ -69,6 +69,8 @@ def lib():
         L.dgw4_forward_timeouts.argtypes = [P, I, I, I, I, I, P, P]
         L.dgw4_sample.restype = I
         L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
+        L.dgw4_pack_tiled.restype = I
+        L.dgw4_pack_tiled.argtypes = [P, I, I, I, I, P, P]
         L.dgw4_hbm_read_probe.restype = I
         L.dgw4_hbm_read_probe.argtypes = [P, S, P, P]
         _lib = L
@@ -129,6 +131,33 @@ def quantize_rtn(w: torch.Tensor, g: int):
     return q, s, z
 
 
+# Or-ed into a weight tuple's group size: q is in the tiled layout of
+# include/dgw4.h (DGW4_WEIGHTS_TILED).
+WEIGHTS_TILED = 0x10000
+
+
+def _group(g: int) -> int:
+    return g & 0xFFFF
+
+
+def pack_tiled(w: tuple) -> tuple:
+    """(q, s, z, g) with q uint8 [..., N, K/2] in the canonical layout ->
+    (qt, s, z, g | WEIGHTS_TILED), qt a new tensor of the same shape in the
+    tiled layout (s and z are shared, not copied). The GEMM entry points take
+    either tuple and give identical results."""
+    q, s, z, g = w
+    if g & WEIGHTS_TILED:
+        raise ValueError("weights are already tiled")
+    pq = _dev(q, "q", (torch.uint8,))
+    *lead, N, K2 = q.shape
+    E = 1
+    for v in lead:
+        E *= v
+    qt = torch.empty_like(q)
+    _check("dgw4_pack_tiled", lib().dgw4_pack_tiled(pq, E, N, 2 * K2, g, qt.data_ptr(), _stream(q)))
+    return qt, s, z, g | WEIGHTS_TILED
+
+
 def forward_timeouts(workspace: torch.Tensor, T: int, topk: int, E: int, d: int, m: int) -> int:
     """How many bounded partner waits of the last moe_forward on ``workspace``
     gave up (0 for every correct launch). Synchronises the current stream."""
@@ -143,11 +172,11 @@ def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> 
     """Dense W4A16 linear: y = x * deq(W)^T.
 
     x fp16 [T, K]; w = (q uint8 [N, K/2], s fp16 [N, K/g], z fp16 [N, K/g], g),
-    e.g. one matrix of quantize_rtn. Returns y fp16 [T, N]."""
+    e.g. one matrix of quantize_rtn, or its pack_tiled form. Returns y fp16 [T, N]."""
     q, s, z, g = w
     T, K = x.shape
     N = q.shape[0]
-    if q.shape != (N, K // 2) or s.shape != (N, K // g) or z.shape != s.shape:
+    if q.shape != (N, K // 2) or s.shape != (N, K // _group(g)) or z.shape != s.shape:
         raise ValueError(f"packed shapes {tuple(q.shape)}, {tuple(s.shape)} do not match x {tuple(x.shape)}")
     px = _dev(x, "x", _F16)
     pq = _dev(q, "q", (torch.uint8,))
@@ -257,7 +286,8 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
 
     x fp16 [T, d]; topk_ids int32 [T, topk]; topk_w fp32 [T, topk];
     gu = (q uint8 [E, 2m, d/2], s fp16 [E, 2m, d/g], z fp16 [E, 2m, d/g], g);
-    dn = (q uint8 [E, d, m/2], s, z, g). Returns out fp16 [T, d].
+    dn = (q uint8 [E, d, m/2], s, z, g). Either tuple may come from
+    pack_tiled (g carries WEIGHTS_TILED). Returns out fp16 [T, d].
     ``workspace`` (uint8 device tensor of at least workspace_bytes(...)) is
     allocated here when not given; pass one to avoid allocation per call.
     ``events``: optional list of 5 torch.cuda.Event(enable_timing=True),
@@ -272,9 +302,9 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
     if gq.shape != (E, 2 * m, d // 2) or dq.shape != (E, d, m // 2):
         raise ValueError(f"packed shapes {tuple(gq.shape)} / {tuple(dq.shape)} do not match "
                          f"x {tuple(x.shape)}")
-    if gs.shape != (E, 2 * m, d // gg) or gz.shape != gs.shape:
+    if gs.shape != (E, 2 * m, d // _group(gg)) or gz.shape != gs.shape:
         raise ValueError("gate_up scale/zero shape mismatch")
-    if ds.shape != (E, d, m // dg) or dz.shape != ds.shape:
+    if ds.shape != (E, d, m // _group(dg)) or dz.shape != ds.shape:
         raise ValueError("down scale/zero shape mismatch")
     if topk_ids.shape != (T, topk) or topk_w.shape != (T, topk):
         raise ValueError("topk_ids / topk_weights must be [T, topk]")

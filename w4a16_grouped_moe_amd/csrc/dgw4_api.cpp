@@ -20,6 +20,23 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool group_supported(int g) { return g == 64 || g == 128; }
 
+// Splits a GEMM group-size argument into the group size and the layout flag;
+// false for flag bits other than DGW4_WEIGHTS_TILED.
+bool split_group(int arg, int &g, int &tiled)
+{
+    if (arg < 0 || (arg & ~(DGW4_WEIGHTS_TILED | 0xFFFF)) != 0)
+        return false;
+    g = arg & 0xFFFF;
+    tiled = (arg & DGW4_WEIGHTS_TILED) != 0;
+    return true;
+}
+
+bool overlap(const void *a, const void *b, size_t bytes)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
 thread_local hipError_t g_last_hip = hipSuccess;   // last failed HIP call of this thread
 
 int from_hip(hipError_t e)
@@ -125,11 +142,14 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
 
 int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                            int T, int topk, int E, int d, int m, const uint8_t *gu_q,
-                           const uint16_t *gu_s, const uint16_t *gu_z, int gu_g,
+                           const uint16_t *gu_s, const uint16_t *gu_z, int gu_garg,
                            const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
-                           int dn_g, void *workspace, size_t *ws_bytes, uint16_t *out,
+                           int dn_garg, void *workspace, size_t *ws_bytes, uint16_t *out,
                            void *stream, void *const *events, int n_events)
 {
+    int gu_g = 0, dn_g = 0, gu_tiled = 0, dn_tiled = 0;
+    if (!split_group(gu_garg, gu_g, gu_tiled) || !split_group(dn_garg, dn_g, dn_tiled))
+        return DGW4_ERR_INVALID_ARG;
     if (events && n_events != 5)
         return DGW4_ERR_INVALID_ARG;
     if (events)
@@ -218,6 +238,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     gu.n_w = 2 * m;
     gu.n_out = m;
     gu.out = h;
+    gu.tiled = gu_tiled;
 
     dn.a_src = h;
     dn.a_rows = (int)cap;
@@ -228,6 +249,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     dn.n_w = d;
     dn.n_out = d;
     dn.out = y;
+    dn.tiled = dn_tiled;
 
     if (dgw4::gate_up_down_fused(gu, gu_g, dn, dn_g)) {
         // one launch for both GEMMs: the stage marks 2 and 3 both follow it
@@ -266,8 +288,11 @@ int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *str
 }
 
 int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
-                      const uint16_t *s, const uint16_t *z, int g, uint16_t *y, void *stream)
+                      const uint16_t *s, const uint16_t *z, int garg, uint16_t *y, void *stream)
 {
+    int g = 0, tiled = 0;
+    if (!split_group(garg, g, tiled))
+        return DGW4_ERR_INVALID_ARG;
     if (T < 0 || K < 2 || (K % 2) != 0 || N < 1 || g < 1)
         return DGW4_ERR_INVALID_ARG;
     if (!group_supported(g))
@@ -300,7 +325,24 @@ int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
     a.A = T;
     a.max_tiles = (T + dgw4::kBlockM - 1) / dgw4::kBlockM;
     a.out = y;
+    a.tiled = tiled;
     return from_hip(dgw4::launch_linear(a, g, (hipStream_t)stream));
+}
+
+int dgw4_pack_tiled(const uint8_t *q, int E, int N, int K, int g, uint8_t *qt, void *stream)
+{
+    if (E < 0 || N < 1 || K < 2 || g < 1)
+        return DGW4_ERR_INVALID_ARG;
+    if (!group_supported(g))
+        return DGW4_ERR_UNSUPPORTED;
+    if (N % 16 != 0 || K % g != 0)
+        return DGW4_ERR_INVALID_ARG;
+    if (E == 0)
+        return DGW4_OK;
+    const size_t bytes = (size_t)E * (size_t)N * (size_t)(K / 2);
+    if (!q || !qt || !aligned(q, 8) || !aligned(qt, 8) || overlap(q, qt, bytes))
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_pack_tiled(q, (long long)E * N, K, g, qt, (hipStream_t)stream));
 }
 
 int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float *entropy, int32_t *sample,

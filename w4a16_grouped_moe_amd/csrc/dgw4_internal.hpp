@@ -19,6 +19,11 @@ constexpr int kMaxExperts = 1024;
 hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t *q,
                                uint16_t *s, uint16_t *z, hipStream_t stream);
 
+// Canonical [rows, K/2] packed weights -> the tiled layout of the GEMM loads
+// ([rows/16][K/g][4][16][g/8]); rows % 16 == 0, K % g == 0, g 64 or 128.
+hipError_t launch_pack_tiled(const uint8_t *q, long long rows, int K, int g, uint8_t *qt,
+                             hipStream_t stream);
+
 // Alignment of the flat assignment ids to experts (one workgroup per
 // expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
 // the tile that hold assignments} for live tiles, {-1, 0} past the total.
@@ -43,7 +48,7 @@ struct GemmArgs {
     int a_rows;                 // rows of a_src (T or cap)
     const int32_t *sorted_ids;  // [cap]
     const int2 *tile_info;      // [cap / kBlockM]: {expert or -1, valid rows}
-    const uint8_t *q;           // packed weights [E, n_w, K/2]
+    const uint8_t *q;           // packed weights [E, n_w, K/2], canonical or tiled (see tiled)
     const uint16_t *s;          // [E, n_w, K/g]
     const uint16_t *z;          // [E, n_w, K/g]
     int K;                      // contraction width (d for gate_up, m for down)
@@ -53,6 +58,7 @@ struct GemmArgs {
     int A;                      // T * topk; also the pad sentinel in sorted_ids
     int max_tiles;              // cap / kBlockM
     void *out;                  // gate_up: H fp16 [cap, m]; down: Y fp16 [A, d]
+    int tiled;                  // 1: q in the tiled layout [E][n_w/16][K/g][4][16][g/8]
 };
 
 hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);

@@ -113,14 +113,44 @@ struct Frag<128> { uint4 v; };   // 16 bytes = 32 nibbles
 template <>
 struct Frag<64> { uint2 v; };    // 8 bytes = 16 nibbles
 
-template <int G>
+// Packed weights come in one of two layouts (the same bytes, reordered):
+//   canonical: q [E, N, K/2], row-major, two nibbles per byte along K;
+//   tiled:     per expert, per 16-row block and per quantisation group, the
+//              16 rows x g/2 bytes of that group stored in the order in which
+//              the MFMA lanes hold them: [E][N/16][K/g][4][16][g/8], i.e.
+//              (quarter q, row r) owns bytes q g/8 .. (q + 1) g/8 of row r's
+//              group. One wave's load of a group is then 8 g contiguous bytes
+//              (whole 128-byte lines), read once and not kept in the caches.
+// Lane (quarter, lrow = lane % 16) of a wave that covers the 16 weight rows
+// row - lrow .. row - lrow + 15 reads its share of group gi at
+// wq_lane_off + wq_group_off(gi) (bytes, from the expert's first byte).
+template <int G, bool TL>
+__device__ inline uint32_t wq_lane_off(int row, int lane, int K)
+{
+    if constexpr (TL)
+        return (uint32_t)(row - (lane & 15)) * (uint32_t)(K / 2) + (uint32_t)(lane * (G / 8));
+    else
+        return (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)((lane >> 4) * (G / 8));
+}
+
+template <int G, bool TL>
+__device__ constexpr uint32_t wq_group_off(int gi)
+{
+    return (uint32_t)gi * (TL ? 8u * G : G / 2u);
+}
+
+// Non-temporal (cache policy nt) for the tiled layout, whose loads cover
+// whole lines; the canonical layout's loads cover half or quarter lines
+// whose rest the next group's load reads, so they stay cacheable.
+template <int G, bool TL>
 __device__ inline Frag<G> load_frag(rsrc_t r, uint32_t voff, uint32_t soff)
 {
+    constexpr int kCpol = TL ? 2 : 0;
     Frag<G> f;
     if constexpr (G == 128)
-        f.v = load16(r, voff, soff);
+        f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpol));
     else
-        f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+        f.v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCpol));
     return f;
 }
 
@@ -240,7 +270,7 @@ constexpr size_t gate_up_lds_bytes_k(int K)
 // GATED: each wave computes a gate column tile and the matching up tile and
 // stores gelu_tanh(gate) * up as H (permuted per 8); otherwise (the dense
 // linear) one column tile, stored as fp16 in natural column order.
-template <int G, int NMS, int NSC, bool GATED>
+template <int G, int NMS, int NSC, bool GATED, bool TL>
 __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                              const int (&fidr)[4])
 {
@@ -308,8 +338,7 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt) {
         lds_row[tt] = tt * kGuCols + wave * 16 + lrow;
-        wvoff[tt] = (uint32_t)((tt ? n_out : 0) + pcol + lrow) * (uint32_t)(K / 2) +
-                    (uint32_t)(quarter * (G / 8));
+        wvoff[tt] = wq_lane_off<G, TL>((tt ? n_out : 0) + pcol + lrow, lane, K);
     }
     Frag<G> bq[P][TT][SG];
     auto issue_w = [&](int st, int s) {           // step s into register stage st
@@ -318,8 +347,8 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
 #pragma unroll
             for (int h = 0; h < SG; ++h) {
                 const int gi = s * SG + h;
-                bq[st][tt][h] = load_frag<G>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
-                                             (uint32_t)(gi * (G / 2)));
+                bq[st][tt][h] = load_frag<G, TL>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
+                                                 wq_group_off<G, TL>(gi));
             }
     };
     // activation slices: thread -> (rows tid / 32 + 8 i, 16-byte segment
@@ -457,7 +486,7 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
     }
 }
 
-template <int G>
+template <int G, bool TL>
 __global__ void __launch_bounds__(kGuThreads)
 __attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
 {
@@ -483,14 +512,14 @@ __attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
         return;
     if (p.K == kGuSteps * 256) {
         if (info.y > 16)
-            gate_up_body<G, 2, kGuSteps, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, kGuSteps, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, kGuSteps, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, kGuSteps, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
     } else {
         if (info.y > 16)
-            gate_up_body<G, 2, 0, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, 0, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, 0, true>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, 0, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
     }
 }
 
@@ -500,7 +529,7 @@ __attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
 // column blocks x, x + 8, ... and runs all row tiles of a block back to back,
 // so the block's weights stream from HBM once and the other row tiles read
 // them from that XCD's L2 (x, at most a few MB, stays in every L2).
-template <int G>
+template <int G, bool TL>
 __global__ void __launch_bounds__(kGuThreads)
 __attribute__((amdgpu_waves_per_eu(3))) linear_kernel(GemmArgs p)
 {
@@ -520,14 +549,14 @@ __attribute__((amdgpu_waves_per_eu(3))) linear_kernel(GemmArgs p)
     const int valid = min(kBlockM, p.A - tile * kBlockM);
     if (p.K == kGuSteps * 256) {
         if (valid > 16)
-            gate_up_body<G, 2, kGuSteps, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, kGuSteps, false, TL>(p, 0, valid, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, kGuSteps, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, kGuSteps, false, TL>(p, 0, valid, tile * kBlockM, cb, fidr);
     } else {
         if (valid > 16)
-            gate_up_body<G, 2, 0, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 2, 0, false, TL>(p, 0, valid, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, 0, false>(p, 0, valid, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, 0, false, TL>(p, 0, valid, tile * kBlockM, cb, fidr);
     }
 }
 
@@ -571,7 +600,7 @@ __device__ inline uint32_t down_a_off(const GemmArgs &p, int row0, int x)
 // CH: groups per K chunk; NCH: chunks per weight tile (both compile-time).
 // EXACT: K = CH * NCH * G exactly (a compile-time constant); otherwise groups
 // past K / G (a rounded-up chunk) read no weights and have scale 0.
-template <int G, int NMS, int CH, int NCH, bool EXACT>
+template <int G, int NMS, int CH, int NCH, bool EXACT, bool TL>
 __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                           const uint4 (&av)[kALoads], int fid)
 {
@@ -631,14 +660,12 @@ __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, i
     Frag<G> bq[P][CH];
     auto issue_w = [&](int st, int u) {
         const int j = u / NCH, c = u % NCH;
-        const uint32_t voff = u < NU && tile_live(j)
-                                  ? (uint32_t)(tile_row(j) + lrow) * (uint32_t)(K / 2) +
-                                        (uint32_t)(quarter * (G / 8))
-                                  : kOutOfRange;
+        const uint32_t voff = u < NU && tile_live(j) ? wq_lane_off<G, TL>(tile_row(j) + lrow, lane, K)
+                                                     : kOutOfRange;
 #pragma unroll
         for (int g = 0; g < CH; ++g) {
             const int gi = c * CH + g;
-            bq[st][g] = load_frag<G>(rq, gi < NG ? voff : kOutOfRange, (uint32_t)(gi * (G / 2)));
+            bq[st][g] = load_frag<G, TL>(rq, gi < NG ? voff : kOutOfRange, wq_group_off<G, TL>(gi));
         }
     };
 
@@ -783,7 +810,7 @@ __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, i
 // Kernel entry for one (tile, column block): the tile's activation rows and
 // assignment ids are requested before its descriptor is known (they depend
 // only on the tile index), then the body for its row count runs.
-template <int G, int CH, int NCH, bool EXACT>
+template <int G, int CH, int NCH, bool EXACT, bool TL>
 __device__ __forceinline__ void down_entry(const GemmArgs &p, int tile, int cb)
 {
     const int tid = threadIdx.x;
@@ -799,12 +826,12 @@ __device__ __forceinline__ void down_entry(const GemmArgs &p, int tile, int cb)
     if (info.x < 0)
         return;
     if (info.y > 16)
-        down_body<G, 2, CH, NCH, EXACT>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+        down_body<G, 2, CH, NCH, EXACT, TL>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
     else
-        down_body<G, 1, CH, NCH, EXACT>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+        down_body<G, 1, CH, NCH, EXACT, TL>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
 }
 
-template <int G>
+template <int G, bool TL>
 __global__ void __launch_bounds__(kDnThreads)
 __attribute__((amdgpu_waves_per_eu(4))) down_kernel(GemmArgs p)
 {
@@ -821,14 +848,14 @@ __attribute__((amdgpu_waves_per_eu(4))) down_kernel(GemmArgs p)
     constexpr int kCh = 768 / G;
     if constexpr (G == 64) {
         if (ng == kDnGroups) {
-            down_entry<G, kDnGroups, 1, true>(p, tile, cb);
+            down_entry<G, kDnGroups, 1, true, TL>(p, tile, cb);
             return;
         }
     }
     if (ng <= kCh)
-        down_entry<G, kCh, 1, false>(p, tile, cb);
+        down_entry<G, kCh, 1, false, TL>(p, tile, cb);
     else
-        down_entry<G, kCh, 2, false>(p, tile, cb);
+        down_entry<G, kCh, 2, false, TL>(p, tile, cb);
 }
 
 // ===========================================================================
@@ -886,7 +913,7 @@ constexpr size_t gate_up4_lds_bytes()
 // H is gathered in LDS and stored at device scope (written through to
 // memory) in whole 16-byte segments: its consumer is the down half of the
 // same launch, on another CU.
-template <int NMS>
+template <int NMS, bool TL>
 __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                               const int (&fidr)[2])
 {
@@ -939,9 +966,7 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
     // pass c: gate rows col0 + 32 wave + 16 c + lrow, then the matching up rows
     auto in_range = [&](int c) { return wave * 32 + c * 16 + lrow; };
-    auto wvoff = [&](int c, int u) {
-        return (uint32_t)((u ? n_out : 0) + col0 + in_range(c)) * (uint32_t)(K / 2) + (uint32_t)(quarter * (G / 8));
-    };
+    auto wvoff = [&](int c, int u) { return wq_lane_off<G, TL>((u ? n_out : 0) + col0 + in_range(c), lane, K); };
     Frag<G> bq[P][2][SG];
     auto issue_w = [&](int st, int q) {            // global step q = 11 pass + step
         const int c = q / kGuSteps, s = q % kGuSteps;
@@ -950,7 +975,7 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
             const uint32_t voff = wvoff(c, u);
 #pragma unroll
             for (int h = 0; h < SG; ++h)
-                bq[st][u][h] = load_frag<G>(rq, voff, (uint32_t)((s * SG + h) * (G / 2)));
+                bq[st][u][h] = load_frag<G, TL>(rq, voff, wq_group_off<G, TL>(s * SG + h));
         }
     };
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
@@ -1122,7 +1147,7 @@ constexpr int vmcnt_at_most(int n)
 // then, once only those loads can still be outstanding, the stores are
 // complete and the half is announced; av is loaded once the counter shows
 // both halves.
-template <int NMS, bool FUSED>
+template <int NMS, bool FUSED, bool TL>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
                                            uint4 (&av)[kDn4ALoads], int fid, int32_t *ready,
                                            int32_t *ready_end)
@@ -1167,12 +1192,10 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     auto tile_row = [&](int j) { return (rt0 + wave + j * kL4Waves) * 16; };   // first weight row
     Frag<G> bq[P][NG];
     auto issue_w = [&](int st, int j) {
-        const uint32_t voff = j < kDn4Tiles ? (uint32_t)(tile_row(j) + lrow) * (uint32_t)(K / 2) +
-                                                  (uint32_t)(quarter * (G / 8))
-                                            : kOutOfRange;
+        const uint32_t voff = j < kDn4Tiles ? wq_lane_off<G, TL>(tile_row(j) + lrow, lane, K) : kOutOfRange;
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            bq[st][g] = load_frag<G>(rq, voff, (uint32_t)(g * (G / 2)));
+            bq[st][g] = load_frag<G, TL>(rq, voff, wq_group_off<G, TL>(g));
     };
 #pragma unroll
     for (int j = 0; j < P; ++j)
@@ -1289,6 +1312,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     }
 }
 
+template <bool TL>
 __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
 {
     // workgroup -> (column half, tile), both halves of a tile on one XCD; the
@@ -1312,9 +1336,9 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     if (info.x < 0)
         return;
     if (info.y > 16)
-        down4_body<2, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+        down4_body<2, false, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
     else
-        down4_body<1, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+        down4_body<1, false, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
 }
 
 // ---- gate_up and down of the layer's shape in one launch. Workgroup (tile,
@@ -1330,6 +1354,7 @@ constexpr size_t layer4_lds_bytes()
     return gate_up4_lds_bytes() > down4_lds_bytes() ? gate_up4_lds_bytes() : down4_lds_bytes();
 }
 
+template <bool TL>
 __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArgs dn, int32_t *ready)
 {
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
@@ -1348,9 +1373,9 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
     if (info.x < 0)
         return;
     if (info.y > 16)
-        gate_up4_body<2>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
+        gate_up4_body<2, TL>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
     else
-        gate_up4_body<1>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
+        gate_up4_body<1, TL>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
     // nothing but the down body's own loads may follow the H stores before
     // it announces the half (it counts them); device-scope fences are not
     // used for that: they would write back and invalidate the whole L2 of
@@ -1358,9 +1383,9 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
     __builtin_amdgcn_sched_barrier(0);
     uint4 av[kDn4ALoads];
     if (info.y > 16)
-        down4_body<2, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
+        down4_body<2, true, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
     else
-        down4_body<1, true>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
+        down4_body<1, true, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
 }
 
 template <class Kern>
@@ -1386,35 +1411,37 @@ bool layer_shape_down(const GemmArgs &a, int g)
     return g == 64 && a.K == kDnGroups * 64 && a.n_out == 2 * kDn4Rows && a.n_w == a.n_out;
 }
 
+template <bool TL>
 hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
 {
-    static size_t allowed = 64 * 1024;
-    hipError_t err = allow_lds(down4_kernel, down4_lds_bytes(), allowed);
+    static size_t allowed = 64 * 1024;             // one per instantiation
+    hipError_t err = allow_lds(down4_kernel<TL>, down4_lds_bytes(), allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
-    down4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes(), stream>>>(a);
+    down4_kernel<TL><<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes(), stream>>>(a);
     return hipGetLastError();
 }
 
+template <bool TL>
 hipError_t launch_layer4(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready, hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;
-    hipError_t err = allow_lds(layer4_kernel, layer4_lds_bytes(), allowed);
+    hipError_t err = allow_lds(layer4_kernel<TL>, layer4_lds_bytes(), allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (gu.max_tiles + kXcds - 1) / kXcds * kXcds;
-    layer4_kernel<<<dim3(tiles * 2), dim3(kL4Threads), layer4_lds_bytes(), stream>>>(gu, dn, ready);
+    layer4_kernel<TL><<<dim3(tiles * 2), dim3(kL4Threads), layer4_lds_bytes(), stream>>>(gu, dn, ready);
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool TL>
 hipError_t launch_linear_g(const GemmArgs &a, hipStream_t stream)
 {
     const int nblocks = (a.n_out + kGuCols - 1) / kGuCols;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    auto kern = linear_kernel<G>;
+    auto kern = linear_kernel<G, TL>;
     static size_t allowed = 64 * 1024;              // raised once per instantiation when needed
     const size_t lds = gate_up_lds_bytes_k<G>(a.K);
     hipError_t err = allow_lds(kern, lds, allowed);
@@ -1427,13 +1454,13 @@ hipError_t launch_linear_g(const GemmArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool TL>
 hipError_t launch_gate_up_g(const GemmArgs &a, hipStream_t stream)
 {
     const int nblocks = (a.n_out + kGuCols - 1) / kGuCols;
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    auto kern = gate_up_kernel<G>;
+    auto kern = gate_up_kernel<G, TL>;
     static size_t allowed = 64 * 1024;              // raised once per instantiation when needed
     const size_t lds = gate_up_lds_bytes_k<G>(a.K);
     hipError_t err = allow_lds(kern, lds, allowed);
@@ -1444,13 +1471,13 @@ hipError_t launch_gate_up_g(const GemmArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int G>
+template <int G, bool TL>
 hipError_t launch_down_g(const GemmArgs &a, hipStream_t stream)
 {
     const int nblocks = (a.n_out / 16 + kDnRows / 16 - 1) / (kDnRows / 16);
     if (a.max_tiles == 0 || nblocks == 0)
         return hipSuccess;
-    auto kern = down_kernel<G>;
+    auto kern = down_kernel<G, TL>;
     static size_t allowed = 64 * 1024;
     const size_t lds = down_lds_bytes_k<G>(a.K);
     hipError_t err = allow_lds(kern, lds, allowed);
@@ -1478,7 +1505,9 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream)
 {
     if (a.max_tiles == 0)
         return hipSuccess;
-    return g == 128 ? launch_gate_up_g<128>(a, stream) : launch_gate_up_g<64>(a, stream);
+    if (a.tiled)
+        return g == 128 ? launch_gate_up_g<128, true>(a, stream) : launch_gate_up_g<64, true>(a, stream);
+    return g == 128 ? launch_gate_up_g<128, false>(a, stream) : launch_gate_up_g<64, false>(a, stream);
 }
 
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
@@ -1486,18 +1515,22 @@ hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
     if (a.max_tiles == 0)
         return hipSuccess;
     if (layer_shape_down(a, g))
-        return launch_down4(a, stream);
-    return g == 128 ? launch_down_g<128>(a, stream) : launch_down_g<64>(a, stream);
+        return a.tiled ? launch_down4<true>(a, stream) : launch_down4<false>(a, stream);
+    if (a.tiled)
+        return g == 128 ? launch_down_g<128, true>(a, stream) : launch_down_g<64, true>(a, stream);
+    return g == 128 ? launch_down_g<128, false>(a, stream) : launch_down_g<64, false>(a, stream);
 }
 
 hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
 {
-    return g == 128 ? launch_linear_g<128>(a, stream) : launch_linear_g<64>(a, stream);
+    if (a.tiled)
+        return g == 128 ? launch_linear_g<128, true>(a, stream) : launch_linear_g<64, true>(a, stream);
+    return g == 128 ? launch_linear_g<128, false>(a, stream) : launch_linear_g<64, false>(a, stream);
 }
 
 bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g)
 {
-    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g);
+    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g) && gu.tiled == dn.tiled;
 }
 
 hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
@@ -1505,7 +1538,9 @@ hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *
 {
     if (gu.max_tiles == 0)
         return hipSuccess;
-    return launch_layer4(gu, dn, ready, stream);
+    if (gu.tiled != dn.tiled)
+        return hipErrorInvalidValue;               // gate_up_down_fused() is false for a mixed pair
+    return gu.tiled ? launch_layer4<true>(gu, dn, ready, stream) : launch_layer4<false>(gu, dn, ready, stream);
 }
 
 }  // namespace dgw4

@@ -72,7 +72,48 @@ __global__ void __launch_bounds__(256) quantize_rtn_kernel(const float2 *__restr
     }
 }
 
+// Canonical -> tiled reorder of packed weights (the GEMMs' load layout): one
+// thread per 8-byte unit of the output, written in order; the source unit is
+// row 16 t + lrow, byte gi g/2 + quarter g/8 + 8 sub of that row. The tiles of
+// all experts follow each other (N is a multiple of 16), so t runs over the
+// whole [E N / 16] stack.
+template <int G>
+__global__ void __launch_bounds__(256) pack_tiled_kernel(const uint2 *__restrict__ q, long long units,
+                                                         int K, uint2 *__restrict__ qt)
+{
+    constexpr int kSub = G / 64;                   // 8-byte units per lane share
+    const long long row_units = K / 16;            // 8-byte units per row
+    const int groups = K / G;
+    for (long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x; u < units;
+         u += (long long)gridDim.x * blockDim.x) {
+        const long long b = u / G;                 // (tile, group) block of 8 G bytes = G units
+        const int w = (int)(u - b * G);
+        const int lane = w / kSub, sub = w - lane * kSub;
+        const long long t = b / groups;
+        const int gi = (int)(b - t * groups);
+        const long long row = t * 16 + (lane & 15);
+        qt[u] = q[row * row_units + gi * (G / 16) + (lane >> 4) * kSub + sub];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pack_tiled(const uint8_t *q, long long rows, int K, int g, uint8_t *qt,
+                             hipStream_t stream)
+{
+    const long long units = rows * (K / 16);
+    if (units == 0)
+        return hipSuccess;
+    const long long want = (units + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+    const uint2 *src = reinterpret_cast<const uint2 *>(q);
+    uint2 *dst = reinterpret_cast<uint2 *>(qt);
+    if (g == 128)
+        pack_tiled_kernel<128><<<dim3(blocks), dim3(256), 0, stream>>>(src, units, K, dst);
+    else
+        pack_tiled_kernel<64><<<dim3(blocks), dim3(256), 0, stream>>>(src, units, K, dst);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t *q,
                                uint16_t *s, uint16_t *z, hipStream_t stream)
