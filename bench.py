@@ -166,6 +166,9 @@ def bench_linear(torch, dg, dev, args) -> int:
     del wd
     y = torch.empty((T, N), dtype=torch.float16, device=dev)
     w = (q, s_, z, g)
+    if args.weight_layout == "tiled":
+        w = dg.pack_tiled(w)
+        del q
     stream = torch.cuda.current_stream(dev)
     for _ in range(max(1, args.warmup // 30)):
         dg.w4a16_linear(xd, w, out=y)
@@ -189,10 +192,12 @@ def bench_linear(torch, dg, dev, args) -> int:
         "warmup": max(1, args.warmup // 30), "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": f"dense W4A16 linear (LM-head shape): T={T}, K={K}, N={N}, g={g}"},
+        "config": {"workload": f"dense W4A16 linear (LM-head shape): T={T}, K={K}, N={N}, g={g}",
+                   "weight_layout": args.weight_layout},
         "us_per_call": round(ms * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
-        "roofline": {"kernel": "linear_kernel<128>", "bound": "hbm", "achieved": round(gbps, 1),
+        "roofline": {"kernel": f"linear_kernel<128, {str(args.weight_layout == 'tiled').lower()}>",
+                     "bound": "hbm", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None},
     }), flush=True)

@@ -11,10 +11,15 @@
 //
 // gfx950 design
 // -------------
-// Weights stream straight from the canonical layout. A lane (row = lane % 16,
-// quarter = lane / 16) loads g/8 bytes of one weight row per group, so the
-// four quarters cover one group of 16 rows; a wave reads whole 128-byte lines
-// of its rows (splitting a line between waves streams markedly slower).
+// A lane (row = lane % 16, quarter = lane / 16) loads g/8 bytes of one weight
+// row per group, so the four quarters cover one group of 16 rows. Weights come
+// in either of two layouts of the same bytes (every kernel is instantiated for
+// both): the canonical one, where those 16 g/2-byte row pieces are half or
+// quarter lines spread over 16 rows, and the tiled one, where they are 8 g
+// contiguous bytes. Only the tiled loads cover whole 128-byte lines, which
+// lets them bypass the caches (non-temporal): the layer then streams its
+// weights about 10% faster. Within a wave the rows' lines are never split with
+// another wave (that streams markedly slower).
 // Dequantisation builds exact fp16 integers in registers: for a word of
 // nibbles n0..n7, (w & 0x000F000F) | 0x64006400 is the fp16 pair (1024 + n0,
 // 1024 + n4) and (w & 0x00F000F0) | 0x54005400 is (64 + n1, 64 + n5); the same
@@ -22,7 +27,7 @@
 // or (64 + z) leaves q - z exactly. The MFMA operand therefore holds K in the
 // order [0,4,1,5,2,6,3,7] per 8; the activations are used in the same order
 // (gate_up permutes x as it stages it, H is written permuted), which leaves
-// the contraction unchanged and needs no weight preshuffle.
+// the contraction unchanged; the nibble order inside a byte never changes.
 // v_mfma_f32_16x16x32_f16 accumulates one group into a fresh fp32 partial and
 // the group's scale is applied once per output in fp32 (acc += s * partial),
 // so no weight is ever rounded by its scale.

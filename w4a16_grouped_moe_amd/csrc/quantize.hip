@@ -1,4 +1,5 @@
-// Min/max round-to-nearest uint4 packer (dg-w4a16-v1 layout).
+// Min/max round-to-nearest uint4 packer (dg-w4a16-v1 layout), and the
+// reorder of its output into the GEMMs' tiled load layout.
 //
 // Follows the "dg-w4-kernels" card, section "W4A16" (quantize_w4 with a group
 // size), the model card's "Benchmarks" (round-to-nearest min/max, no
