@@ -134,3 +134,12 @@ def test_linear_tiled_equals_canonical(g, T, K, N):
     tiled = dg.w4a16_linear(xd, _tiled((q, s, z, g)))
     torch.cuda.synchronize()
     assert torch.equal(tiled.view(torch.int16), canon.view(torch.int16))
+
+
+def test_forward_tiled_skew_bitexact_sampled():
+    # Zipf-skewed routing: hot experts span many tiles (their tiled weights
+    # are read through the caches), cold ones one tile (read past them)
+    L = lc.build(CONFIGS["skew"])
+    out = _forward_pair(L)
+    toks = np.sort(np.random.default_rng(9).choice(L.shape.T, 12, replace=False)).astype(np.int32)
+    lc.assert_close(out[toks], lc.oracle_forward(L, tokens=toks), "tiled skew (sampled 12 tokens)")

@@ -136,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
     for (int t = off / bm + tid; t < (off + padded) / bm; t += kThreads) {
         tile_expert[t] = e;
         if (tile_info)
-            tile_info[t] = make_int2(e, min(bm, cnt - (t * bm - off)));
+            tile_info[t] = make_int2(e, min(bm, cnt - (t * bm - off)) | min(padded / bm, 0x7FFF) << 16);
     }
     if (tid == 0) {
         counts[e] = cnt;

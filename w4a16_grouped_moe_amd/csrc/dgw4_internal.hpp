@@ -24,9 +24,16 @@ hipError_t launch_quantize_rtn(const float *w, long long groups, int g, uint8_t 
 hipError_t launch_pack_tiled(const uint8_t *q, long long rows, int K, int g, uint8_t *qt,
                              hipStream_t stream);
 
+// A tile descriptor tile_info[j] = {expert or -1, y}: y holds the tile's
+// valid rows in bits 0..15 and, in bits 16..30, how many tiles its expert
+// has (capped at 0x7FFF; only "one" or "more" is used).
+__host__ __device__ constexpr int tile_valid(int y) { return y & 0xFFFF; }
+__host__ __device__ constexpr int tile_count(int y) { return y >> 16; }
+
 // Alignment of the flat assignment ids to experts (one workgroup per
 // expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
-// the tile that hold assignments} for live tiles, {-1, 0} past the total.
+// the tile that hold assignments | tiles of the expert << 16} for live tiles,
+// {-1, 0} past the total.
 // ready (may be null) gets n_ready zeros: the per-tile counters of the fused
 // gate_up + down launch that follows.
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,

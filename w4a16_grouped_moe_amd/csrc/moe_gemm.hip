@@ -144,13 +144,15 @@ __device__ constexpr uint32_t wq_group_off(int gi)
     return (uint32_t)gi * (TL ? 8u * G : G / 2u);
 }
 
-// Non-temporal (cache policy nt) for the tiled layout, whose loads cover
-// whole lines; the canonical layout's loads cover half or quarter lines
-// whose rest the next group's load reads, so they stay cacheable.
-template <int G, bool TL>
+// NT: non-temporal (cache policy nt). Only for the tiled layout, whose loads
+// cover whole lines, and only where no other workgroup will read the same
+// weights (an expert with a single tile): the canonical layout's loads cover
+// half or quarter lines whose rest the next group's load reads, and the
+// other tiles of a busy expert re-read its weights from the caches.
+template <int G, bool NT>
 __device__ inline Frag<G> load_frag(rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    constexpr int kCpol = TL ? 2 : 0;
+    constexpr int kCpol = NT ? 2 : 0;
     Frag<G> f;
     if constexpr (G == 128)
         f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCpol));
@@ -352,7 +354,7 @@ __device__ __forceinline__ void gate_up_body(const GemmArgs &p, int e, int valid
 #pragma unroll
             for (int h = 0; h < SG; ++h) {
                 const int gi = s * SG + h;
-                bq[st][tt][h] = load_frag<G, TL>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
+                bq[st][tt][h] = load_frag<G, false>(rq, gi < NG ? wvoff[tt] : kOutOfRange,
                                                  wq_group_off<G, TL>(gi));
             }
     };
@@ -512,19 +514,20 @@ __attribute__((amdgpu_waves_per_eu(3))) gate_up_kernel(GemmArgs p)
 #pragma unroll
     for (int i = 0; i < 4; ++i)                   // < cap: always in the buffer
         fidr[i] = p.sorted_ids[tile * kBlockM + r0 + i * (kGuThreads / kStepSeg)];
-    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    const int2 info = p.tile_info[tile];           // {expert, valid rows | tiles << 16}; -1 past the total
     if (info.x < 0)
         return;
+    const int valid = tile_valid(info.y);
     if (p.K == kGuSteps * 256) {
-        if (info.y > 16)
-            gate_up_body<G, 2, kGuSteps, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+        if (valid > 16)
+            gate_up_body<G, 2, kGuSteps, true, TL>(p, info.x, valid, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, kGuSteps, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, kGuSteps, true, TL>(p, info.x, valid, tile * kBlockM, cb, fidr);
     } else {
-        if (info.y > 16)
-            gate_up_body<G, 2, 0, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+        if (valid > 16)
+            gate_up_body<G, 2, 0, true, TL>(p, info.x, valid, tile * kBlockM, cb, fidr);
         else
-            gate_up_body<G, 1, 0, true, TL>(p, info.x, info.y, tile * kBlockM, cb, fidr);
+            gate_up_body<G, 1, 0, true, TL>(p, info.x, valid, tile * kBlockM, cb, fidr);
     }
 }
 
@@ -670,7 +673,7 @@ __device__ __forceinline__ void down_body(const GemmArgs &p, int e, int valid, i
 #pragma unroll
         for (int g = 0; g < CH; ++g) {
             const int gi = c * CH + g;
-            bq[st][g] = load_frag<G, TL>(rq, gi < NG ? voff : kOutOfRange, wq_group_off<G, TL>(gi));
+            bq[st][g] = load_frag<G, false>(rq, gi < NG ? voff : kOutOfRange, wq_group_off<G, TL>(gi));
         }
     };
 
@@ -827,13 +830,14 @@ __device__ __forceinline__ void down_entry(const GemmArgs &p, int tile, int cb)
     int fid = 0;
     if (tid < kBlockM)
         fid = p.sorted_ids[tile * kBlockM + tid];
-    const int2 info = p.tile_info[tile];           // {expert, valid rows}; -1 past the total
+    const int2 info = p.tile_info[tile];           // {expert, valid rows | tiles << 16}; -1 past the total
     if (info.x < 0)
         return;
-    if (info.y > 16)
-        down_body<G, 2, CH, NCH, EXACT, TL>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+    const int valid = tile_valid(info.y);
+    if (valid > 16)
+        down_body<G, 2, CH, NCH, EXACT, TL>(p, info.x, valid, tile * kBlockM, cb, av, fid);
     else
-        down_body<G, 1, CH, NCH, EXACT, TL>(p, info.x, info.y, tile * kBlockM, cb, av, fid);
+        down_body<G, 1, CH, NCH, EXACT, TL>(p, info.x, valid, tile * kBlockM, cb, av, fid);
 }
 
 template <int G, bool TL>
@@ -918,7 +922,7 @@ constexpr size_t gate_up4_lds_bytes()
 // H is gathered in LDS and stored at device scope (written through to
 // memory) in whole 16-byte segments: its consumer is the down half of the
 // same launch, on another CU.
-template <int NMS, bool TL>
+template <int NMS, bool TL, bool NT>
 __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
                                               const int (&fidr)[2])
 {
@@ -980,7 +984,7 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
             const uint32_t voff = wvoff(c, u);
 #pragma unroll
             for (int h = 0; h < SG; ++h)
-                bq[st][u][h] = load_frag<G, TL>(rq, voff, wq_group_off<G, TL>(s * SG + h));
+                bq[st][u][h] = load_frag<G, NT>(rq, voff, wq_group_off<G, TL>(s * SG + h));
         }
     };
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
@@ -1152,7 +1156,7 @@ constexpr int vmcnt_at_most(int n)
 // then, once only those loads can still be outstanding, the stores are
 // complete and the half is announced; av is loaded once the counter shows
 // both halves.
-template <int NMS, bool FUSED, bool TL>
+template <int NMS, bool FUSED, bool TL, bool NT>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
                                            uint4 (&av)[kDn4ALoads], int fid, int32_t *ready,
                                            int32_t *ready_end)
@@ -1200,7 +1204,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
         const uint32_t voff = j < kDn4Tiles ? wq_lane_off<G, TL>(tile_row(j) + lrow, lane, K) : kOutOfRange;
 #pragma unroll
         for (int g = 0; g < NG; ++g)
-            bq[st][g] = load_frag<G, TL>(rq, voff, wq_group_off<G, TL>(g));
+            bq[st][g] = load_frag<G, NT>(rq, voff, wq_group_off<G, TL>(g));
     };
 #pragma unroll
     for (int j = 0; j < P; ++j)
@@ -1340,10 +1344,18 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     const int2 info = p.tile_info[tile];
     if (info.x < 0)
         return;
-    if (info.y > 16)
-        down4_body<2, false, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
-    else
-        down4_body<1, false, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+    const bool more = tile_valid(info.y) > 16;
+    if (TL && tile_count(info.y) == 1) {
+        if (more)
+            down4_body<2, false, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+        else
+            down4_body<1, false, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+    } else {
+        if (more)
+            down4_body<2, false, TL, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+        else
+            down4_body<1, false, TL, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+    }
 }
 
 // ---- gate_up and down of the layer's shape in one launch. Workgroup (tile,
@@ -1377,20 +1389,47 @@ __global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArg
     const int2 info = gu.tile_info[tile];
     if (info.x < 0)
         return;
-    if (info.y > 16)
-        gate_up4_body<2, TL>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
-    else
-        gate_up4_body<1, TL>(gu, info.x, info.y, tile * kBlockM, cb, fidr);
+    const int valid = tile_valid(info.y);
+    // tiled weights of an expert that no other tile reads stream past the
+    // caches; those of an expert with several tiles stay cacheable
+    const bool nt = TL && tile_count(info.y) == 1;
+    // (the distinct asm statements keep the compiler from hoisting the two
+    // gate_up arms' common prologue above the branch, which spills)
+    if (valid > 16) {
+        if (nt) {
+            asm volatile("; streaming weights");
+            gate_up4_body<2, TL, TL>(gu, info.x, valid, tile * kBlockM, cb, fidr);
+        } else {
+            asm volatile("; cached weights");
+            gate_up4_body<2, TL, false>(gu, info.x, valid, tile * kBlockM, cb, fidr);
+        }
+    } else {
+        if (nt) {
+            asm volatile("; streaming weights");
+            gate_up4_body<1, TL, TL>(gu, info.x, valid, tile * kBlockM, cb, fidr);
+        } else {
+            asm volatile("; cached weights");
+            gate_up4_body<1, TL, false>(gu, info.x, valid, tile * kBlockM, cb, fidr);
+        }
+    }
     // nothing but the down body's own loads may follow the H stores before
     // it announces the half (it counts them); device-scope fences are not
     // used for that: they would write back and invalidate the whole L2 of
     // the XCD, stalling every other workgroup streaming through it
     __builtin_amdgcn_sched_barrier(0);
     uint4 av[kDn4ALoads];
-    if (info.y > 16)
-        down4_body<2, true, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
-    else
-        down4_body<1, true, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, ready + gu.max_tiles);
+    int32_t *const timeouts = ready + gu.max_tiles;
+    if (valid > 16) {
+        if (nt)
+            down4_body<2, true, TL, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
+        else
+            down4_body<2, true, TL, false>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
+    } else {
+        if (nt)
+            down4_body<1, true, TL, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
+        else
+            down4_body<1, true, TL, false>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
+    }
 }
 
 template <class Kern>
