@@ -85,10 +85,17 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
     for (int j = 0; j < kPer; ++j)
         if (v[j] >= 0 && v[j] < E)
             atomicAdd(&s_cnt[v[j]], 1);
-    for (int i = kChunk + tid; i < A; i += kThreads) {
-        const int u = ids[i];
-        if (u >= 0 && u < E)
-            atomicAdd(&s_cnt[u], 1);
+    for (int c0 = kChunk; c0 < A; c0 += kChunk) {  // later chunks: loads issued together
+        int u[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = c0 + j * kThreads + tid;
+            u[j] = i < A ? ids[i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            if (u[j] >= 0 && u[j] < E)
+                atomicAdd(&s_cnt[u[j]], 1);
     }
     __syncthreads();
 
