@@ -53,6 +53,11 @@ CONFIGS = {
     "skew": LayerShape("skew", 2, E=128, topk=8, T=256, d=2816, m=704, zipf=1.2),
     "stack": LayerShape("stack", 3, E=128, topk=8, T=256, d=2816, m=704, layers=30),
     "wide": LayerShape("wide", 4, E=128, topk=8, T=1024, d=2816, m=704),
+    # the down projection with g = 64 at K = 704 (gate_up at g = 64, so the
+    # two GEMMs run as separate launches) against the pages' variant with
+    # g = 128 and K padded to 768: timing cases for the down stage
+    "down_g64": LayerShape("down_g64", 5, E=128, topk=8, T=256, d=2816, m=704, g_gu=64),
+    "down_g128": LayerShape("down_g128", 6, E=128, topk=8, T=256, d=2816, m=768, g_gu=64, g_dn=128),
 }
 
 

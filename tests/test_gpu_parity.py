@@ -283,3 +283,11 @@ def test_read_probe_runs():
     gbps = n / (e0.elapsed_time(e1) * 1e-3) / 1e9
     lc.log(f"[probe] 64 MiB read at {gbps:.0f} GB/s")
     assert sink.item() == 0 and gbps > 100.0
+
+
+@pytest.mark.parametrize("name", ["down_g64", "down_g128"])
+def test_forward_down_group_variants_sampled(name):
+    # the layer's shape with separate gate_up and down launches: down at
+    # g = 64 (K = 704) and the g = 128 variant with K padded to 768
+    L = lc.build(CONFIGS[name])
+    _sampled(L, 12, 5, f"{name} (sampled 12 tokens)")
