@@ -50,6 +50,8 @@ def load():
         lib.orc_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                         P, P, P, I, P, P, P, I, P, I, P, P]
         lib.orc_philox4x32_10.argtypes = [P, P, P]
+        lib.orc_gumbel_uniform.restype = ctypes.c_float
+        lib.orc_gumbel_uniform.argtypes = [ctypes.c_uint32]
         lib.orc_gumbel_score.restype = ctypes.c_float
         lib.orc_gumbel_score.argtypes = [ctypes.c_float, I, I, ctypes.c_uint64]
         lib.orc_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P]
@@ -122,22 +124,6 @@ def dequant(q, s, z, g: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("orc_dequant: invalid shape")
     return out
-
-
-def pack_tiled(q, g: int) -> np.ndarray:
-    """The library's tiled layout of packed weights: the bytes of q
-    [..., N, K/2] reordered as [..., N/16, K/g, 4, 16, g/8], i.e. blocks of 16
-    rows, then the groups along K, then the four quarters of a group's g/2
-    bytes, then the 16 rows, then the g/8 bytes of one quarter. No page
-    defines this layout (it is the gfx950 GEMMs' load order); it is written
-    here as the reshape and axis transposition it is."""
-    q = np.asarray(q)
-    *lead, N, KB = q.shape
-    assert N % 16 == 0 and (2 * KB) % g == 0
-    v = q.reshape(*lead, N // 16, 16, KB // (g // 2), 4, g // 8)
-    n = len(lead)
-    axes = list(range(n)) + [n, n + 2, n + 3, n + 1, n + 4]
-    return np.ascontiguousarray(v.transpose(axes)).reshape(q.shape)
 
 
 def align(ids, E: int, block_m: int) -> dict:
@@ -214,6 +200,11 @@ def philox4x32_10(ctr, key) -> np.ndarray:
     out = np.empty(4, np.uint32)
     load().orc_philox4x32_10(_p(c), _p(k), _p(out))
     return out
+
+
+def gumbel_uniform(w: int) -> float:
+    """The uniform in (0, 1) the sampler derives from one 32-bit Philox word."""
+    return float(load().orc_gumbel_uniform(int(w) & 0xFFFFFFFF))
 
 
 def gumbel_score(l: float, r: int, v: int, seed: int) -> float:

@@ -474,17 +474,24 @@ void orc_philox4x32_10(const uint32_t *ctr, const uint32_t *key, uint32_t *out)
  * kernel card's "noise comes from Philox inline"; the pages do not fix the
  * stream): the Philox block with counter {v / 4, r, 0, 0} and key
  * {seed low 32 bits, seed high 32 bits}, its word v % 4 as w; the uniform
- * U = (w / 256 + 1/2) / 2^24 in (0, 1), exact in fp32; the standard Gumbel
- * variate G = -log(-log U); score = l + G. Everything after the integer step
- * is fp32 (the precision the GPU kernel takes the decision in).
+ * U = (floor(w / 2^9) + 1/2) / 2^23 from the top 23 bits of w, an exact fp32
+ * number in [2^-24, 1 - 2^-24] (never 0 or 1, so the score is always
+ * finite); the standard Gumbel variate G = -log(-log U); score = l + G.
+ * Everything after the integer step is fp32 (the precision the GPU kernel
+ * takes the decision in).
  */
+float orc_gumbel_uniform(uint32_t w)
+{
+    return ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
+}
+
 float orc_gumbel_score(float l, int r, int v, uint64_t seed)
 {
     const uint32_t ctr[4] = {(uint32_t)v >> 2, (uint32_t)r, 0u, 0u};
     const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
     uint32_t w[4];
     orc_philox4x32_10(ctr, key, w);
-    const float u = ((float)(w[v & 3] >> 8) + 0.5f) * (1.0f / 16777216.0f);
+    const float u = orc_gumbel_uniform(w[v & 3]);
     const float g = -logf(-logf(u));
     return l + g;
 }

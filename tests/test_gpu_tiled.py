@@ -1,7 +1,7 @@
 """GPU: the tiled weight layout (include/dgw4.h, "Tiled weight layout").
 
-dgw4_pack_tiled is compared byte for byte with the oracle's definition of the
-layout; every GEMM entry point given tiled weights must give results
+dgw4_pack_tiled is compared byte for byte with the tests' description of the
+layout (tests/tiled_layout.py); every GEMM entry point given tiled weights must give results
 bit-identical to the same call on the canonical weights (the same arithmetic
 in the same order, only the load addresses differ), and the layer output is
 also checked against the oracle on the shapes each kernel family covers.
@@ -15,6 +15,7 @@ import w4a16_grouped_moe_amd as dg
 from synth import CONFIGS
 from synth.inputs import linear_inputs
 from tests import layer_cases as lc
+from tests.tiled_layout import pack_tiled
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +28,10 @@ def _need_gpu():
 
 
 def _tiled(w):
-    """Device pack -> tiled pack, checked against the oracle's layout."""
+    """Device pack -> tiled pack, checked against the layout's description."""
     t = dg.pack_tiled(w)
     torch.cuda.synchronize()
-    want = oracle.pack_tiled(w[0].cpu().numpy(), w[3])
+    want = pack_tiled(w[0].cpu().numpy(), w[3])
     assert np.array_equal(t[0].cpu().numpy(), want), "tiled bytes differ from the layout"
     return t
 

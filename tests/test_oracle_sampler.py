@@ -93,3 +93,56 @@ def test_gumbel_sample_properties():
     a = oracle.sample(lg2, 1)[1]
     assert np.array_equal(a, oracle.sample(lg2, 1)[1])
     assert not np.array_equal(a, oracle.sample(lg2, 2)[1])
+
+
+def test_masked_entropy_matches_scipy():
+    # -inf logits are masked entries (probability 0): the entropy is that of
+    # the softmax over the live entries only, and a row with one live entry
+    # has entropy exactly 0
+    rng = np.random.default_rng(14)
+    V = 777
+    lg = (rng.standard_normal((5, V)) * 3.0).astype(np.float32)
+    lg[0, ::3] = -np.inf
+    lg[1, : V - 2] = -np.inf                          # two live entries
+    lg[2, :] = -np.inf
+    lg[2, 400] = 1.25                                 # one live entry
+    lg[3, rng.choice(V, V // 2, replace=False)] = -np.inf
+    h, smp, am, sc = oracle.sample(lg, 5)
+    for r in range(lg.shape[0]):
+        live = np.isfinite(lg[r])
+        x = lg[r, live].astype(np.float64)
+        p = np.exp(x - x.max())
+        p /= p.sum()
+        assert abs(h[r] - scipy.stats.entropy(p)) < 1e-9 * max(1.0, abs(h[r])), r
+        assert np.isfinite(lg[r, am[r]]) and am[r] == int(np.argmax(lg[r]))
+        assert np.isfinite(lg[r, smp[r]]), "a masked entry was sampled"
+        assert np.isfinite(sc[r])
+    assert h[2] == 0.0 and am[2] == 400 and smp[2] == 400
+
+
+def test_gumbel_uniform_is_exact_and_open():
+    # U = (floor(w / 2^9) + 1/2) 2^-23 must be exact in fp32 and strictly
+    # inside (0, 1) for every 32-bit word, including both extremes, so that
+    # -log(-log U) is always finite
+    words = [0, 1, 511, 512, 0x7FFFFFFF, 0x80000000, 0xFFFFFE00, 0xFFFFFFFF]
+    rng = np.random.default_rng(15)
+    words += [int(v) for v in rng.integers(0, 2**32, 2000, dtype=np.uint64)]
+    for w in words:
+        u = oracle.gumbel_uniform(w)
+        want = ((w >> 9) + 0.5) / 2.0**23            # exact in float64
+        assert u == want, hex(w)
+        assert 0.0 < u < 1.0, hex(w)
+        g = -np.log(-np.log(np.float32(u)))           # the variate, in fp32
+        assert np.isfinite(g), hex(w)
+    assert oracle.gumbel_uniform(0xFFFFFFFF) == 1.0 - 2.0**-24
+    assert oracle.gumbel_uniform(0) == 2.0**-24
+
+
+def test_gumbel_scores_finite_on_a_large_row():
+    # every score of a long row is finite (no word maps to U = 0 or 1)
+    V = 1 << 16
+    lg = np.zeros((2, V), np.float32)
+    _, _, _, sc = oracle.sample(lg, 123)
+    assert np.all(np.isfinite(sc))
+    for v in range(0, V, 4099):
+        assert np.isfinite(oracle.gumbel_score(0.0, 1, v, 123))

@@ -1,8 +1,8 @@
-"""Pins of the oracle's tiled weight layout (CPU only).
+"""Checks of the tests' description of the tiled weight layout (CPU only).
 
 The layout is this library's own (include/dgw4.h, "Tiled weight layout"):
-qt[b][j][p][r][i] = q[16 b + r][j g/2 + p g/8 + i]. The oracle writes it as a
-reshape and transposition; here it is checked element by element against
+qt[b][j][p][r][i] = q[16 b + r][j g/2 + p g/8 + i]. The test helper writes it
+as a reshape and transposition; here it is checked element by element against
 that index formula on small stacks, and against the property the GEMMs rely
 on: one wave's load of group j of a 16-row block (8 g contiguous bytes) holds
 exactly those rows' bytes of that group, lane (p, r) at offset (16 p + r) g/8.
@@ -10,7 +10,7 @@ exactly those rows' bytes of that group, lane (p, r) at offset (16 p + r) g/8.
 import numpy as np
 import pytest
 
-import oracle
+from tests.tiled_layout import pack_tiled
 
 
 @pytest.mark.parametrize("g", [64, 128])
@@ -19,7 +19,7 @@ def test_tiled_index_formula(g, lead):
     N, K = 32, 3 * g
     size = int(np.prod(lead, dtype=np.int64)) * N * (K // 2)
     q = np.arange(size, dtype=np.int64).reshape(*lead, N, K // 2)   # every byte its own id
-    qt = oracle.pack_tiled(q, g)
+    qt = pack_tiled(q, g)
     assert qt.shape == q.shape
     flat_q = q.reshape(-1, N, K // 2)
     flat_t = qt.reshape(-1, N * (K // 2))
@@ -41,7 +41,7 @@ def test_tiled_wave_loads(g):
     rng = np.random.default_rng(5)
     E, N, K = 2, 48, 4 * g
     q = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
-    qt = oracle.pack_tiled(q, g).reshape(E, -1)
+    qt = pack_tiled(q, g).reshape(E, -1)
     share = g // 8
     for e in range(E):
         for b in range(N // 16):

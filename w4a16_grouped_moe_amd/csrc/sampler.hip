@@ -10,9 +10,10 @@
 //
 // Noise: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011), one block
 // per four consecutive logits of a row: counter {v / 4, row, 0, 0}, key
-// {seed low word, seed high word}; word v % 4 gives the uniform
-// U = (w / 256 + 1/2) / 2^24 (exact in fp32) and G = -log(-log U); the sample
-// is the first v with the largest l_v + G_v, all in fp32.
+// {seed low word, seed high word}; the top 23 bits of word v % 4 give the
+// uniform U = (floor(w / 512) + 1/2) / 2^23, exact in fp32 and strictly
+// inside (0, 1), and G = -log(-log U); the sample is the first v with the
+// largest l_v + G_v, all in fp32.
 //
 // Layout: workgroup (split, row) streams a contiguous slice of the row with
 // non-temporal 16-byte loads (each wave instruction covers whole lines) and
@@ -65,13 +66,16 @@ __device__ inline void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint
     out[3] = c3;
 }
 
-// G = -log(-log U) through the hardware base-2 logarithm (v_log_f32):
-// U is in [2^-25, 1 - 2^-25] and -log U in [2.9e-8, 17.4], both normal, so
-// no range handling is needed; its error is below one ulp of the score.
+// G = -log(-log U) through the hardware base-2 logarithm (v_log_f32).
+// U = (floor(w / 2^9) + 1/2) 2^-23 takes 23 bits so that every value is an
+// exact fp32 number: it lies in [2^-24, 1 - 2^-24], never 0 or 1 (24 bits
+// would round the top value, 2^24 - 1/2, up to 2^24 and give U = 1, an
+// infinite score). -log U is then in [6.0e-8, 16.7], both ends normal, so no
+// range handling is needed; the log's error is below one ulp of the score.
 __device__ inline float gumbel(uint32_t w)
 {
     constexpr float kLn2 = 0.693147180559945309f;
-    const float u = ((float)(w >> 8) + 0.5f) * (1.0f / 16777216.0f);
+    const float u = ((float)(w >> 9) + 0.5f) * (1.0f / 8388608.0f);
     const float e = -kLn2 * __builtin_amdgcn_logf(u);
     return -kLn2 * __builtin_amdgcn_logf(e);
 }
