@@ -27,6 +27,7 @@ import numpy as np
 
 METRIC = "µs/MoE layer + achieved HBM GB/s (% of 8 TB/s), T=256, 128e top-8 W4A16"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0     # dense fp16 MFMA, MI355X
 # The pages' GB10 figure for one W4 MoE layer at M=256 (Part 2 blog, "Start
 # with the measured machine"): 2.366 ms. As GB/s on this layer's algorithmic
 # bytes it is context from another machine, not a target.
@@ -50,10 +51,14 @@ def layer_bytes(shape, populated: int) -> dict:
     x = T * d * 2
     out = T * d * 2
     route = A * 4 * 2                                                 # ids + weights
+    # the GEMM launches' algorithmic bytes: the packed weights of the
+    # populated experts plus the activations they read from the caller (x);
+    # the workspace traffic of H, Y and the sorted ids is implementation
+    # overhead and not counted
     return dict(
         layer=populated * (gu_w + dn_w) + x + out + route,
-        gate_up=populated * gu_w + x + A * m * 2,                    # + H written (fp16)
-        down=populated * dn_w + A * m * 2 + A * d * 2,               # H read + Y written (fp16)
+        gate_up=populated * gu_w + x,
+        down=populated * dn_w,
         weights=populated * (gu_w + dn_w),
     )
 
@@ -73,11 +78,19 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic() -> dict | None:
-    """HBM bytes per launch of the two GEMM kernels from the committed counter
+def traffic_key(shape, layout: str) -> dict:
+    """What a counter record must have been taken on to describe this run."""
+    return {"T": shape.T, "E": shape.E, "topk": shape.topk, "d": shape.d, "m": shape.m,
+            "g_gu": shape.g_gu, "g_dn": shape.g_dn,
+            "routing": f"zipf({shape.zipf})" if shape.zipf else "uniform", "layout": layout}
+
+
+def measured_traffic(key: dict) -> dict | None:
+    """HBM bytes per launch of the GEMM kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads
-    for a plain copy of known size), or None when the GEMM sources changed
-    since the counters were taken."""
+    for a plain copy of known size), or None when no record was taken on this
+    workload (token count, routing, weight layout) or the GEMM sources
+    changed since the counters were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), TRAFFIC_PROFILE)
     try:
         text = open(path).read()
@@ -86,10 +99,38 @@ def measured_traffic() -> dict | None:
     m = re.search(r"```json\n(.*?)\n```", text, re.S)
     if not m:
         return None
-    rec = json.loads(m.group(1))
-    if rec.get("source_sha256") != gemm_source_hash():
-        return None
-    return rec
+    recs = json.loads(m.group(1))
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if rec.get("source_sha256") == gemm_source_hash() and rec.get("workload") == key:
+            return rec
+    return None
+
+
+def make_layer(torch, dg, shape, l: int, dev, layout: str = "tiled", keep_masters: bool = False) -> dict:
+    """Layer l of a workload as the benchmark runs it: fp32 master weights
+    drawn on the device (seeded), packed there by dgw4_quantize_rtn, the
+    tiled copies made by dgw4_pack_tiled (a load-time conversion, outside
+    every timed region), activations and routing from the host generators.
+    ``gu``/``dn`` are the packs in ``layout``, ``gu_other``/``dn_other`` the
+    other layout's. keep_masters also returns the fp32 masters (on the
+    device), for auditing a layer against the oracle."""
+    from synth import activations, expert_weights_device, routing
+    gw, dw = expert_weights_device(shape, l, dev)
+    gu_c = (*dg.quantize_rtn(gw, shape.g_gu), shape.g_gu)
+    dn_c = (*dg.quantize_rtn(dw, shape.g_dn), shape.g_dn)
+    masters = (gw, dw) if keep_masters else None
+    del gw, dw
+    gu_t, dn_t = dg.pack_tiled(gu_c), dg.pack_tiled(dn_c)
+    tiled = layout == "tiled"
+    x = activations(shape, l)
+    ids, w = routing(shape, l)
+    populated = int(np.unique(ids).size)
+    return dict(
+        gu=gu_t if tiled else gu_c, dn=dn_t if tiled else dn_c,
+        gu_other=gu_c if tiled else gu_t, dn_other=dn_c if tiled else dn_t,
+        x=torch.from_numpy(x).to(dev), ids=torch.from_numpy(ids).to(dev),
+        w=torch.from_numpy(w).to(dev), bytes=layer_bytes(shape, populated),
+        populated=populated, masters=masters, x_host=x, ids_host=ids, w_host=w)
 
 
 def graph_replay(torch, dg, step, L, R, out, last, ws, dev) -> dict:
@@ -185,7 +226,9 @@ def bench_linear(torch, dg, dev, args) -> int:
     wbytes = N * K // 2 + 2 * N * (K // g) * 2
     nbytes = wbytes + T * K * 2 + T * N * 2
     gbps = nbytes / (ms * 1e-3) / 1e9
-    log(f"[linear] {steps} calls: {ms * 1e3:.1f} us each, {gbps:.1f} GB/s")
+    flops = 2 * T * K * N
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"[linear] {steps} calls: {ms * 1e3:.1f} us each, {gbps:.1f} GB/s, {tflops:.1f} TFLOP/s")
     print(json.dumps({
         "metric": "us per dense W4A16 linear + achieved HBM GB/s (% of 8 TB/s)",
         "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -196,10 +239,13 @@ def bench_linear(torch, dg, dev, args) -> int:
                    "weight_layout": args.weight_layout},
         "us_per_call": round(ms * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
+        # 2 T K N FLOP over 392 MB of weights is 4 T = 1024 FLOP per byte,
+        # far past the fp16 ridge (2.5 PFLOP/s over 8 TB/s = 312): MFMA-bound
         "roofline": {"kernel": f"linear_kernel<128, {str(args.weight_layout == 'tiled').lower()}>",
-                     "bound": "hbm", "achieved": round(gbps, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                     "flops_per_call": flops, "traffic": None},
     }), flush=True)
     return 0
 
@@ -253,8 +299,16 @@ def bench_sampler(torch, dg, dev, args) -> int:
     return 0
 
 
-def cpu_baseline(shape):
-    """The CPU oracle, as it stands, on one full layer drawn on the host."""
+CPU_SAMPLE_TOKENS = 16
+
+
+def cpu_baseline(shape, runs: int = 3):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: the
+    first CPU_SAMPLE_TOKENS tokens of one full layer drawn on the host (all
+    their top-k assignments through the full-size experts), timed as the
+    median of `runs` runs at one thread and at every core this process may
+    use. The rate is scaled to the whole layer (the oracle's work is linear
+    in the tokens): layer bytes / (sample seconds x T / sample tokens)."""
     import oracle
     from synth import activations, expert_weights, routing
     t0 = time.time()
@@ -265,17 +319,34 @@ def cpu_baseline(shape):
     del dw
     x = activations(shape, 0)
     ids, w = routing(shape, 0)
-    log(f"[cpu] inputs ready in {time.time() - t0:.1f}s; timing the oracle forward")
-    t1 = time.perf_counter()
-    oracle.moe_forward(x, ids, w, gu, dn, shape.E)
-    sec = time.perf_counter() - t1
+    toks = np.arange(CPU_SAMPLE_TOKENS, dtype=np.int32)
     populated = int(np.unique(ids).size)
-    gbps = layer_bytes(shape, populated)["layer"] / sec / 1e9
-    log(f"[cpu] oracle: {sec:.2f} s per layer ({gbps:.3f} GB/s) on {oracle.threads()} threads")
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"one full layer (T={shape.T}, all tokens, E={shape.E}, top-{shape.topk}, "
-                      f"d={shape.d}, m={shape.m}) drawn on the host; {sec:.2f} s per layer",
-            "seconds_per_layer": round(sec, 3)}
+    nbytes = layer_bytes(shape, populated)["layer"]
+    log(f"[cpu] inputs ready in {time.time() - t0:.1f}s; timing the oracle forward")
+    all_cores = len(os.sched_getaffinity(0))
+    legs = {}
+    for n in (1, all_cores):
+        used = oracle.set_threads(n)
+        secs = []
+        for _ in range(runs):
+            t1 = time.perf_counter()
+            oracle.moe_forward(x, ids, w, gu, dn, shape.E, tokens=toks)
+            secs.append(time.perf_counter() - t1)
+        sec = float(np.median(secs))
+        layer_sec = sec * shape.T / CPU_SAMPLE_TOKENS
+        legs[n] = dict(value=round(nbytes / layer_sec / 1e9, 4), cores=used,
+                       sample_seconds=[round(v, 3) for v in secs],
+                       seconds_per_layer=round(layer_sec, 3))
+        log(f"[cpu] oracle on {used} threads: {sec:.2f} s per {CPU_SAMPLE_TOKENS}-token sample "
+            f"(median of {runs}), {layer_sec:.2f} s per layer, {legs[n]['value']} GB/s")
+    top = legs[all_cores]
+    return {"value": top["value"], "unit": "GB/s", "cores": top["cores"], "kind": "oracle",
+            "sample": (f"the first {CPU_SAMPLE_TOKENS} of {shape.T} tokens of one full layer "
+                       f"(E={shape.E}, top-{shape.topk}, d={shape.d}, m={shape.m}) drawn on the "
+                       f"host; median of {runs} runs, scaled to the whole layer"),
+            "seconds_per_layer": top["seconds_per_layer"],
+            "sample_seconds": top["sample_seconds"],
+            "one_thread": legs[1]}
 
 
 def main() -> int:
@@ -305,7 +376,7 @@ def main() -> int:
 
     import torch
     import w4a16_grouped_moe_amd as dg
-    from synth import CONFIGS, activations, expert_weights_device, routing
+    from synth import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm device", file=sys.stderr)
@@ -332,26 +403,7 @@ def main() -> int:
         L = max(1, args.layers)          # rotate weight sets for single-layer workloads too
 
     t0 = time.time()
-    layers = []
-    for l in range(L):
-        gw, dw = expert_weights_device(shape, l, dev)
-        gu_c = (*dg.quantize_rtn(gw, shape.g_gu), shape.g_gu)
-        del gw
-        dn_c = (*dg.quantize_rtn(dw, shape.g_dn), shape.g_dn)
-        del dw
-        # the tiled copies: the same bytes in the GEMMs' load order (a
-        # load-time conversion, outside every timed region)
-        gu_t, dn_t = dg.pack_tiled(gu_c), dg.pack_tiled(dn_c)
-        tiled = args.weight_layout == "tiled"
-        x = activations(shape, l)
-        ids, w = routing(shape, l)
-        populated = int(np.unique(ids).size)
-        layers.append(dict(
-            gu=gu_t if tiled else gu_c, dn=dn_t if tiled else dn_c,
-            gu_other=gu_c if tiled else gu_t, dn_other=dn_c if tiled else dn_t,
-            x=torch.from_numpy(x).to(dev), ids=torch.from_numpy(ids).to(dev),
-            w=torch.from_numpy(w).to(dev), bytes=layer_bytes(shape, populated),
-            populated=populated))
+    layers = [make_layer(torch, dg, shape, l, dev, args.weight_layout) for l in range(L)]
     torch.cuda.synchronize()
     log(f"[bench] {L} layers packed on the device in {time.time() - t0:.1f}s "
         f"({sum(x['bytes']['weights'] for x in layers) / 1e9:.2f} GB of packed weights touched)")
@@ -447,7 +499,7 @@ def main() -> int:
 
     probe = read_probe(torch, dg, dev)
     probe["pct_of_probe"] = round(100 * gbps / probe["gbps"], 2)
-    traffic = measured_traffic()
+    traffic = measured_traffic(traffic_key(shape, args.weight_layout))
     pages_gbps = layers[0]["bytes"]["layer"] / (GB10_LAYER_MS * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -495,7 +547,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gemm_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": traffic["layer4"]["bytes_per_launch"] if traffic and fused else None,
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
             "bytes_per_launch": layers[0]["bytes"]["gate_up"] + layers[0]["bytes"]["down"],
             "us_per_launch": round(float(gemm_ms * 1e3 / S), 2),
         },

@@ -24,6 +24,7 @@ from .api import (  # noqa: F401
     moe_forward,
     gelu_tanh,
     threads,
+    set_threads,
     philox4x32_10,
     gumbel_uniform,
     gumbel_score,

@@ -50,6 +50,8 @@ def load():
         lib.orc_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                         P, P, P, I, P, P, P, I, P, I, P, P]
         lib.orc_philox4x32_10.argtypes = [P, P, P]
+        lib.orc_set_threads.restype = I
+        lib.orc_set_threads.argtypes = [I]
         lib.orc_gumbel_uniform.restype = ctypes.c_float
         lib.orc_gumbel_uniform.argtypes = [ctypes.c_uint32]
         lib.orc_gumbel_score.restype = ctypes.c_float
@@ -63,11 +65,13 @@ def load():
 
 
 def threads() -> int:
-    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS or all cores)."""
-    env = os.environ.get("OMP_NUM_THREADS")
-    if env and env.isdigit():
-        return int(env)
-    return len(os.sched_getaffinity(0))
+    """Threads the oracle's OpenMP loops use now."""
+    return int(load().orc_set_threads(0))
+
+
+def set_threads(n: int) -> int:
+    """Set the threads of the oracle's OpenMP loops; returns the count in force."""
+    return int(load().orc_set_threads(int(n)))
 
 
 def _p(a: np.ndarray):

@@ -31,9 +31,19 @@
  * expert.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads of the OpenMP loops below (for timing the oracle at a given core
+ * count); returns the count now in force. */
+int orc_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+    return omp_get_max_threads();
+}
 
 /* ---------------------------------------------------------------- fp16 ---- */
 

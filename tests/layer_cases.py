@@ -61,10 +61,12 @@ def pack_both(wf: np.ndarray, g: int):
     return (hq, hs, hz, g), (dq, ds, dz, g)
 
 
-def build(shape: LayerShape, layer: int = 0, ids=None, w=None) -> Layer:
+def build(shape: LayerShape, layer: int = 0, ids=None, w=None, weights=None) -> Layer:
+    """weights: optional fp32 masters (gate_up [E, 2m, d], down [E, d, m]) in
+    place of the seeded ones."""
     log(f"[layer] building {shape.name} T={shape.T} E={shape.E} topk={shape.topk} "
         f"d={shape.d} m={shape.m} layer={layer}")
-    gw, dw = expert_weights(shape, layer)
+    gw, dw = expert_weights(shape, layer) if weights is None else weights
     gu_h, gu_d = pack_both(gw, shape.g_gu)
     del gw
     dn_h, dn_d = pack_both(dw, shape.g_dn)
@@ -74,6 +76,17 @@ def build(shape: LayerShape, layer: int = 0, ids=None, w=None) -> Layer:
         ids, w = routing(shape, layer)
     return Layer(shape, x, ids, w, gu_h, dn_h, gu_d, dn_d,
                  _to_dev(x), _to_dev(ids.astype(np.int32)), _to_dev(w.astype(np.float32)))
+
+
+_CACHE: dict = {}
+
+
+def cached(name: str) -> Layer:
+    """The named workload's layer 0, built once per test process (the
+    full-size layers take seconds to draw and pack on the host)."""
+    if name not in _CACHE:
+        _CACHE[name] = build(CONFIGS[name])
+    return _CACHE[name]
 
 
 def custom_shape(name, E, topk, T, d, m, g_gu=128, g_dn=64, zipf=None, index=90):
