@@ -168,10 +168,13 @@ DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int blo
  *   out[t] = sum over k = 0..topk-1 (ascending) of
  *            w[t,k] * down_e( gelu_tanh(gate_e(x[t])) * up_e(x[t] ) ),  e = ids[t,k]
  * with expert weights dequantised as w = (q - z) * s. Accumulation is fp32;
- * the gated intermediate and each expert output are rounded to fp16 once,
- * and the combine sums w[t,k] * output in ascending k in fp32 without
- * atomics, then rounds once to fp16. Repeated calls on the same inputs give bit-identical
- * results.
+ * the gated intermediate and each expert output are rounded to fp16 once
+ * (at the layer's shape, d = 2816, m = 704, gate_up g = 128, down g = 64,
+ * each expert output is kept as two fp16 partials, one per half of down's
+ * contraction, added in fp32 by the combine), and the combine sums
+ * w[t,k] * output in ascending k in fp32 without atomics, then rounds once
+ * to fp16. No workgroup waits for another and nothing depends on timing:
+ * repeated calls on the same inputs give bit-identical results.
  *
  *   x          device fp16 bits [T, d]
  *   topk_ids   device int32 [T, topk]; ids outside [0, E) contribute nothing
@@ -202,14 +205,16 @@ DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const 
  * dgw4_moe_forward_timed — dgw4_moe_forward with stage events, for per-kernel
  * timing of the same launch sequence (same kernels, same arguments, same
  * results). events is an array of n_events = 5 caller-created hipEvent_t
- * handles (passed as void*); they are recorded on `stream` before the
- * alignment kernel and after each of the four stages (align, gate_up, down,
- * combine). Elapsed time between consecutive events is the duration of one
- * stage. Where gate_up and down run as one launch (d = 2816, m = 704,
- * gate_up g = 128, down g = 64), events 2 and 3 are both recorded after that
- * launch and the down stage brackets no kernel. events == NULL behaves exactly like dgw4_moe_forward; any other
- * n_events is DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL)
- * records nothing.
+ * handles (passed as void*); they are recorded on `stream` before the first
+ * kernel and after each of the four stages (align, gate_up, down, combine).
+ * Elapsed time between consecutive events is the duration of one stage.
+ * Where alignment, gate_up and down run as one launch (the layer's shape:
+ * d = 2816, m = 704, gate_up g = 128, down g = 64, both stacks in the same
+ * layout), events 1, 2 and 3 are all recorded after that launch, so the
+ * first stage brackets it and the next two bracket no kernel. events == NULL
+ * behaves exactly like dgw4_moe_forward; any other n_events is
+ * DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL) records
+ * nothing.
  */
 DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     const float *topk_w, int T, int topk, int E, int d, int m,
@@ -220,18 +225,19 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     void *stream, void *const *events, int n_events);
 
 /*
- * dgw4_forward_timeouts — a diagnostic for dgw4_moe_forward at the layer's
- * shape, where gate_up and down run as one launch and each workgroup waits,
- * with a bounded number of polls, for the other half of its tile's H. Writes
- * to *timeouts (host memory) how many such waits of the last forward on
- * `workspace` reached the bound (0 for every correct launch; a nonzero count
- * means that forward's output is not to be trusted). T, topk, E, d, m: as
- * passed to that forward. Unlike the other calls this one synchronises
- * `stream` (it copies one word to the host). DGW4_ERR_INVALID_ARG for null
- * pointers or invalid sizes, DGW4_ERR_HIP if the copy fails.
+ * dgw4_moe_experts — the expert stages of dgw4_moe_forward alone (alignment,
+ * gate_up with its activation, down), without the combine: the same kernels
+ * with the same arguments, leaving each assignment's expert output in the
+ * workspace instead of reducing them into out. A measurement aid (timing the
+ * expert kernels back to back without the combine), not a step a layer
+ * needs on its own. Arguments, checks and workspace as for dgw4_moe_forward
+ * (the same workspace size); topk_w and out are not taken.
  */
-DGW4_API int dgw4_forward_timeouts(const void *workspace, int T, int topk, int E, int d, int m,
-                                   int32_t *timeouts, void *stream);
+DGW4_API int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T, int topk, int E,
+                              int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
+                              const uint16_t *gu_z, int gu_g, const uint8_t *dn_q,
+                              const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
+                              void *workspace, size_t *ws_bytes, void *stream);
 
 /*
  * dgw4_w4a16_linear — the dense W4A16 linear layer: y = x * deq(W)^T
@@ -263,7 +269,8 @@ DGW4_API int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uin
  *   argmax[r]  = the first v with the largest logit;
  *   sample[r]  = the first v with the largest l_v + G_v, a draw from
  *                Categorical(p) by Gumbel-max. G_v = -log(-log U_v) in fp32;
- *                U_v = (w / 256 + 1/2) / 2^24 with w word v % 4 of the
+ *                U_v = (floor(w / 512) + 1/2) / 2^23, exact in fp32 and
+ *                strictly inside (0, 1), with w word v % 4 of the
  *                Philox4x32-10 block with counter {v / 4, r, 0, 0} and key
  *                {seed & 0xffffffff, seed >> 32}. Same seed, same draw.
  * logits: device, row-major [R, V], 16-byte aligned, finite or -inf (masked,

@@ -34,8 +34,8 @@ def test_align_capacity():
 def test_workspace_query():
     n = dg.workspace_bytes(256, 8, 128, 2816, 704)
     cap = 256 * 8 + 128 * 31
-    # H fp16 [cap, m] + Y fp16 [A, d] + alignment buffers
-    data = cap * 704 * 2 + 2048 * 2816 * 2
+    # H fp16 [cap, m] + two fp16 partials of Y [2][A, d] + alignment buffers
+    data = cap * 704 * 2 + 2 * 2048 * 2816 * 2
     assert data <= n < data + 64 * 1024
     assert n % 256 == 0
 
@@ -141,15 +141,22 @@ def test_sample_workspace_and_rejects():
     assert f(None, 0, 1024, 1, None, None, None, p, ctypes.byref(big), None) == B.OK   # R = 0
 
 
-def test_forward_timeouts_rejects():
+def test_moe_experts_checks_like_forward():
     import ctypes
-    f = dg.lib().dgw4_forward_timeouts
-    out = ctypes.c_int32(0)
+    f = dg.lib().dgw4_moe_experts
+    n = ctypes.c_size_t(0)
+    # workspace query: the forward's size
+    assert f(None, None, 256, 8, 128, 2816, 704, None, None, None, 128, None, None, None, 64,
+             None, ctypes.byref(n), None) == B.OK
+    assert n.value == dg.workspace_bytes(256, 8, 128, 2816, 704)
+    assert f(None, None, 256, 8, 128, 2816, 704, None, None, None, 96, None, None, None, 64,
+             None, ctypes.byref(n), None) == B.ERR_UNSUPPORTED
+    assert f(None, None, 256, 9, 8, 2816, 704, None, None, None, 128, None, None, None, 64,
+             None, ctypes.byref(n), None) == B.ERR_INVALID_ARG           # topk > E
     p = 1 << 12
-    assert f(None, 256, 8, 128, 2816, 704, ctypes.byref(out), None) == B.ERR_INVALID_ARG
-    assert f(p, 256, 8, 128, 2816, 704, None, None) == B.ERR_INVALID_ARG
-    assert f(p, -1, 8, 128, 2816, 704, ctypes.byref(out), None) == B.ERR_INVALID_ARG
-
+    big = ctypes.c_size_t(1 << 30)
+    assert f(None, p, 4, 8, 128, 2816, 704, p, p, p, 128, p, p, p, 64,
+             p, ctypes.byref(big), None) == B.ERR_INVALID_ARG            # x null
 
 
 def test_pack_tiled_rejects():

@@ -112,16 +112,13 @@ def test_forward_tiled_full_deterministic_100():
     gu, dn = dg.pack_tiled(L.gu_dev), dg.pack_tiled(L.dn_dev)
     first = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, workspace=ws).clone()
     bad = 0
-    timeouts = []
     for i in range(100):
         if i % 10 == 0:
             ws.random_(0, 256)
         o = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, workspace=ws)
         bad += int(not torch.equal(o.view(torch.int16), first.view(torch.int16)))
-        timeouts.append(dg.forward_timeouts(ws, sh.T, sh.topk, sh.E, sh.d, sh.m))
-    lc.log(f"[tiled] full: 100 runs, {bad} differing, timeouts {sum(timeouts)}")
+    lc.log(f"[tiled] full: 100 runs, {bad} differing")
     assert bad == 0
-    assert timeouts == [0] * 100
 
 
 def test_forward_tiled_unfused_layer_shape():

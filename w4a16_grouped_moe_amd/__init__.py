@@ -21,6 +21,6 @@ from .binding import (  # noqa: F401
     w4a16_linear,
     sample,
     fused_entropy,
-    forward_timeouts,
+    moe_experts,
     gumbel_argmax_sample,
 )

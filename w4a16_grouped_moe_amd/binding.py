@@ -65,8 +65,9 @@ def lib():
                                              ctypes.POINTER(P), I]
         L.dgw4_w4a16_linear.restype = I
         L.dgw4_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P, P]
-        L.dgw4_forward_timeouts.restype = I
-        L.dgw4_forward_timeouts.argtypes = [P, I, I, I, I, I, P, P]
+        L.dgw4_moe_experts.restype = I
+        L.dgw4_moe_experts.argtypes = [P, P, I, I, I, I, I, P, P, P, I, P, P, P, I,
+                                       P, ctypes.POINTER(S), P]
         L.dgw4_sample.restype = I
         L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
         L.dgw4_pack_tiled.restype = I
@@ -156,16 +157,6 @@ def pack_tiled(w: tuple) -> tuple:
     qt = torch.empty_like(q)
     _check("dgw4_pack_tiled", lib().dgw4_pack_tiled(pq, E, N, 2 * K2, g, qt.data_ptr(), _stream(q)))
     return qt, s, z, g | WEIGHTS_TILED
-
-
-def forward_timeouts(workspace: torch.Tensor, T: int, topk: int, E: int, d: int, m: int) -> int:
-    """How many bounded partner waits of the last moe_forward on ``workspace``
-    gave up (0 for every correct launch). Synchronises the current stream."""
-    pws = _dev(workspace, "workspace", (torch.uint8,))
-    out = ctypes.c_int32(-1)
-    _check("dgw4_forward_timeouts", lib().dgw4_forward_timeouts(
-        pws, T, topk, E, d, m, ctypes.byref(out), _stream(workspace)))
-    return int(out.value)
 
 
 def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -337,3 +328,26 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
             ptrs[3], ptrs[4], ptrs[5], gg, ptrs[6], ptrs[7], ptrs[8], dg,
             pws, ctypes.byref(n), pout, _stream(x), ev, 5))
     return out
+
+
+def moe_experts(x: torch.Tensor, topk_ids: torch.Tensor, gu: tuple, dn: tuple,
+                workspace: torch.Tensor) -> None:
+    """The expert stages of moe_forward alone (alignment, gate_up, down; no
+    combine), leaving the expert outputs in ``workspace``: a measurement aid
+    for timing those kernels back to back (see dgw4_moe_experts)."""
+    gq, gs, gz, gg = gu
+    dq, ds, dz, dg = dn
+    T, d = x.shape
+    topk = topk_ids.shape[1]
+    E = gq.shape[0]
+    m = dq.shape[2] * 2
+    if gq.shape != (E, 2 * m, d // 2) or dq.shape != (E, d, m // 2) or topk_ids.shape != (T, topk):
+        raise ValueError("shapes do not match")
+    ptrs = [_dev(x, "x", _F16), _dev(topk_ids, "topk_ids", (torch.int32,)),
+            _dev(gq, "gu_q", (torch.uint8,)), _dev(gs, "gu_s", _F16), _dev(gz, "gu_z", _F16),
+            _dev(dq, "dn_q", (torch.uint8,)), _dev(ds, "dn_s", _F16), _dev(dz, "dn_z", _F16)]
+    pws = _dev(workspace, "workspace", (torch.uint8,))
+    n = ctypes.c_size_t(workspace.numel())
+    _check("dgw4_moe_experts", lib().dgw4_moe_experts(
+        ptrs[0], ptrs[1], T, topk, E, d, m, ptrs[2], ptrs[3], ptrs[4], gg,
+        ptrs[5], ptrs[6], ptrs[7], dg, pws, ctypes.byref(n), _stream(x)))

@@ -18,6 +18,8 @@
 //      ({expert, rows of the tile that hold assignments} descriptors too);
 //      workgroup 0 also writes the totals and fills the buffers past the
 //      total (sentinel ids, tiles marked -1).
+// The layer kernel at the layer's shape repeats steps 1-3 for its own tile
+// inside its workgroups; this kernel serves dgw4_align and the other shapes.
 // Ids outside [0, E) are skipped everywhere. The result depends only on the
 // ids, never on timing.
 #include "dgw4_internal.hpp"
@@ -62,8 +64,7 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
                                                         int32_t *__restrict__ sorted_ids,
                                                         int32_t *__restrict__ tile_expert,
                                                         int32_t *__restrict__ num_padded,
-                                                        int2 *__restrict__ tile_info,
-                                                        int32_t *__restrict__ ready, int n_ready)
+                                                        int2 *__restrict__ tile_info)
 {
     __shared__ int32_t s_cnt[kMaxExperts];
     __shared__ int32_t s_wsum[kWaves];
@@ -161,9 +162,6 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
             if (tile_info)
                 tile_info[t] = make_int2(-1, 0);
         }
-        if (ready)
-            for (int t = tid; t < n_ready; t += kThreads)
-                ready[t] = 0;
     }
 }
 
@@ -172,11 +170,11 @@ __global__ void __launch_bounds__(kThreads) align_kernel(const int32_t *__restri
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
-                        int32_t *ready, int n_ready, hipStream_t stream)
+                        hipStream_t stream)
 {
     align_kernel<<<dim3(E), dim3(kThreads), 0, stream>>>(topk_ids, A, E, block_m, (int)cap,
                                                          counts, offsets, sorted_ids, tile_expert,
-                                                         num_padded, tile_info, ready, n_ready);
+                                                         num_padded, tile_info);
     return hipGetLastError();
 }
 

@@ -47,11 +47,14 @@ int from_hip(hipError_t e)
     return DGW4_ERR_HIP;
 }
 
-// Workspace of one forward call: alignment buffers, per-tile counters of the
-// fused GEMM launch, the gated intermediate H (fp16, one row per padded assignment) and the
-// per-assignment expert outputs Y (fp16, one row per flat assignment id).
+// Workspace of one forward call: alignment buffers, the gated intermediate H
+// (fp16, one row per padded assignment) and the per-assignment expert outputs
+// Y (fp16, one row per flat assignment id; two such arrays, the partials of
+// the two halves of down's contraction, at the layer's shape). The layer
+// kernel aligns inside its workgroups and keeps H in LDS, so at the layer's
+// shape only Y is used.
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, tile_info, ready, sorted_ids, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap)
@@ -68,10 +71,9 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
     L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
-    L.ready = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM + 1));   // + the timeout count
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
-    L.y = take(sizeof(uint16_t) * (size_t)A * (size_t)d);
+    L.y = take(2 * sizeof(uint16_t) * (size_t)A * (size_t)d);
     L.total = off;
     return L;
 }
@@ -137,15 +139,21 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_align(topk_ids, T * topk, E, block_m, (long long)cap, counts,
                                        offsets, sorted_ids, tile_expert, num_padded, nullptr,
-                                       nullptr, 0, (hipStream_t)stream));
+                                       (hipStream_t)stream));
 }
 
-int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
-                           int T, int topk, int E, int d, int m, const uint8_t *gu_q,
-                           const uint16_t *gu_s, const uint16_t *gu_z, int gu_garg,
-                           const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
-                           int dn_garg, void *workspace, size_t *ws_bytes, uint16_t *out,
-                           void *stream, void *const *events, int n_events)
+namespace {
+
+// The forward (with_combine) or its expert stages alone; events (5 or null)
+// are recorded before the first kernel and after each stage: alignment,
+// gate_up, down, combine. At the layer's shape the first three are one
+// launch, recorded by marks 1, 2 and 3 together after it.
+int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *topk_w, int T,
+                     int topk, int E, int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
+                     const uint16_t *gu_z, int gu_garg, const uint8_t *dn_q, const uint16_t *dn_s,
+                     const uint16_t *dn_z, int dn_garg, void *workspace, size_t *ws_bytes,
+                     uint16_t *out, void *stream, void *const *events, int n_events,
+                     bool with_combine)
 {
     int gu_g = 0, dn_g = 0, gu_tiled = 0, dn_tiled = 0;
     if (!split_group(gu_garg, gu_g, gu_tiled) || !split_group(dn_garg, dn_g, dn_tiled))
@@ -174,7 +182,7 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
         dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds || m > dgw4::down_max_k() ||
         d / gu_g > dgw4::gate_up_max_groups())
         return DGW4_ERR_UNSUPPORTED;
-    // the GEMMs address x, H and one expert's packed weights with 32-bit offsets
+    // the GEMMs address x, H, Y and one expert's packed weights with 32-bit offsets
     if ((long long)T * d * 2 >= (1LL << 31) || (long long)cap * m * 2 >= (1LL << 31) ||
         (long long)2 * m * d / 2 >= (1LL << 31))
         return DGW4_ERR_UNSUPPORTED;
@@ -185,11 +193,11 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     }
     if (!gu_q || !gu_s || !gu_z || !dn_q || !dn_s || !dn_z)
         return DGW4_ERR_INVALID_ARG;
-    if (T > 0 && (!x || !topk_ids || !topk_w || !out))
+    if (T > 0 && (!x || !topk_ids || (with_combine && (!topk_w || !out))))
         return DGW4_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign) || !aligned(x, 16) || !aligned(gu_q, 16) ||
         !aligned(dn_q, 16) || !aligned(gu_s, 16) || !aligned(gu_z, 16) || !aligned(dn_s, 16) ||
-        !aligned(dn_z, 16) || !aligned(out, 8))
+        !aligned(dn_z, 16) || (with_combine && !aligned(out, 8)))
         return DGW4_ERR_INVALID_ARG;
     if (*ws_bytes < L.total)
         return DGW4_ERR_WORKSPACE;
@@ -206,20 +214,9 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
     int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
-    int32_t *ready = reinterpret_cast<int32_t *>(ws + L.ready);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
-
-    hipError_t err = mark(0);
-    if (err == hipSuccess)
-        err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
-                                 offsets, sorted_ids, tile_expert, num_padded, tile_info, ready,
-                                 (int)(cap / dgw4::kBlockM) + 1, st);
-    if (err == hipSuccess)
-        err = mark(1);
-    if (err != hipSuccess)
-        return from_hip(err);
 
     dgw4::GemmArgs gu{};
     gu.sorted_ids = sorted_ids;
@@ -251,22 +248,48 @@ int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const flo
     dn.out = y;
     dn.tiled = dn_tiled;
 
-    if (dgw4::gate_up_down_fused(gu, gu_g, dn, dn_g)) {
-        // one launch for both GEMMs: the stage marks 2 and 3 both follow it
-        if ((err = dgw4::launch_gate_up_down(gu, dn, ready, st)) != hipSuccess ||
-            (err = mark(2)) != hipSuccess || (err = mark(3)) != hipSuccess)
+    hipError_t err = mark(0);
+    if (err != hipSuccess)
+        return from_hip(err);
+    const bool fused = dgw4::layer_fused(gu, gu_g, dn, dn_g, E);
+    if (fused) {
+        // alignment, gate_up and down in one launch: marks 1, 2 and 3 all follow it
+        if ((err = dgw4::launch_layer(gu, dn, topk_ids, E, st)) != hipSuccess ||
+            (err = mark(1)) != hipSuccess || (err = mark(2)) != hipSuccess ||
+            (err = mark(3)) != hipSuccess)
             return from_hip(err);
     } else {
+        if ((err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
+                                      offsets, sorted_ids, tile_expert, num_padded, tile_info,
+                                      st)) != hipSuccess ||
+            (err = mark(1)) != hipSuccess)
+            return from_hip(err);
         if ((err = dgw4::launch_gate_up(gu, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
             return from_hip(err);
         if ((err = dgw4::launch_down(dn, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
             return from_hip(err);
     }
-
-    if ((err = dgw4::launch_combine(y, topk_ids, topk_w, T, topk, E, d, out, st)) != hipSuccess ||
+    if (!with_combine)
+        return DGW4_OK;
+    if ((err = dgw4::launch_combine(y, fused ? 2 : 1, topk_ids, topk_w, T, topk, E, d, out, st)) !=
+            hipSuccess ||
         (err = mark(4)) != hipSuccess)
         return from_hip(err);
     return DGW4_OK;
+}
+
+}  // namespace
+
+int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
+                           int T, int topk, int E, int d, int m, const uint8_t *gu_q,
+                           const uint16_t *gu_s, const uint16_t *gu_z, int gu_garg,
+                           const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
+                           int dn_garg, void *workspace, size_t *ws_bytes, uint16_t *out,
+                           void *stream, void *const *events, int n_events)
+{
+    return moe_forward_impl(x, topk_ids, topk_w, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_garg, dn_q,
+                            dn_s, dn_z, dn_garg, workspace, ws_bytes, out, stream, events, n_events,
+                            true);
 }
 
 int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w, int T,
@@ -275,9 +298,18 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
                      const uint16_t *dn_z, int dn_g, void *workspace, size_t *ws_bytes,
                      uint16_t *out, void *stream)
 {
-    return dgw4_moe_forward_timed(x, topk_ids, topk_w, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g,
-                                  dn_q, dn_s, dn_z, dn_g, workspace, ws_bytes, out, stream,
-                                  nullptr, 0);
+    return moe_forward_impl(x, topk_ids, topk_w, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g, dn_q,
+                            dn_s, dn_z, dn_g, workspace, ws_bytes, out, stream, nullptr, 0, true);
+}
+
+int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T, int topk, int E, int d,
+                     int m, const uint8_t *gu_q, const uint16_t *gu_s, const uint16_t *gu_z,
+                     int gu_g, const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
+                     int dn_g, void *workspace, size_t *ws_bytes, void *stream)
+{
+    return moe_forward_impl(x, topk_ids, nullptr, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g, dn_q,
+                            dn_s, dn_z, dn_g, workspace, ws_bytes, nullptr, stream, nullptr, 0,
+                            false);
 }
 
 int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream)
@@ -365,24 +397,6 @@ int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float *entropy
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_sample(logits, R, V, seed, entropy, sample, argmax, workspace,
                                         (hipStream_t)stream));
-}
-
-int dgw4_forward_timeouts(const void *workspace, int T, int topk, int E, int d, int m,
-                          int32_t *timeouts, void *stream)
-{
-    if (!workspace || !timeouts || T < 0 || topk < 1 || E < 1 || d < 1 || m < 1)
-        return DGW4_ERR_INVALID_ARG;
-    const size_t cap = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
-    if (cap == 0)
-        return DGW4_ERR_INVALID_ARG;
-    const Layout L = layout((long long)T * topk, T, E, d, m, (long long)cap);
-    const char *slot = static_cast<const char *>(workspace) + L.ready +
-                       sizeof(int32_t) * (cap / dgw4::kBlockM);
-    hipStream_t st = (hipStream_t)stream;
-    hipError_t err = hipMemcpyAsync(timeouts, slot, sizeof(int32_t), hipMemcpyDeviceToHost, st);
-    if (err == hipSuccess)
-        err = hipStreamSynchronize(st);
-    return from_hip(err);
 }
 
 }  // extern "C"

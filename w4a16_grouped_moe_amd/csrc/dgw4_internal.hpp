@@ -34,12 +34,10 @@ __host__ __device__ constexpr int tile_count(int y) { return y >> 16; }
 // expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
 // the tile that hold assignments | tiles of the expert << 16} for live tiles,
 // {-1, 0} past the total.
-// ready (may be null) gets n_ready zeros: the per-tile counters of the fused
-// gate_up + down launch that follows.
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
-                        int32_t *ready, int n_ready, hipStream_t stream);
+                        hipStream_t stream);
 
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
@@ -76,12 +74,14 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
 
-// Whether the pair of GEMMs runs as one launch (the layer's shape), and that
-// launch: ready holds one zeroed counter per tile (gu.max_tiles of them) and
-// one more, ready[gu.max_tiles], that counts partner waits which gave up.
-bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g);
-hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
-                               hipStream_t stream);
+// Whether alignment and the pair of GEMMs run as one launch (the layer's
+// shape), and that launch. It reads the expert ids itself (gu.sorted_ids and
+// gu.tile_info are unused) and writes dn.out as two fp16 partials
+// [2][A][n_out], one per half of down's contraction, to be added by the
+// combine (launch_combine with halves = 2).
+bool layer_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g, int E);
+hipError_t launch_layer(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,
+                        hipStream_t stream);
 
 // Sampler: splits per row, workspace bytes, and the two launches (partials,
 // then the per-row merge). V is a multiple of 4; any output may be null
@@ -95,7 +95,10 @@ hipError_t launch_sample(const float *logits, int R, int V, uint64_t seed, float
 // dgw4_hbm_read_probe.
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
-hipError_t launch_combine(const uint16_t *y, const int32_t *topk_ids, const float *topk_w,
-                          int T, int topk, int E, int d, uint16_t *out, hipStream_t stream);
+// y: `halves` (1 or 2) fp16 arrays [T * topk, d] one after the other; each
+// assignment's expert output is their sum.
+hipError_t launch_combine(const uint16_t *y, int halves, const int32_t *topk_ids,
+                          const float *topk_w, int T, int topk, int E, int d, uint16_t *out,
+                          hipStream_t stream);
 
 }  // namespace dgw4

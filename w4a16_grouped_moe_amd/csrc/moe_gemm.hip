@@ -42,29 +42,25 @@
 //
 // Activation rows re-read from L2 share each CU's vector-memory path with the
 // weight stream and measurably lower it, so the layer's shape (d = 2816,
-// m = 704, gate_up g = 128, down g = 64) takes wide-block bodies run as one
-// 11-wave workgroup per CU (2 per 32-row tile, 256 for the 128 tiles of a
-// 256-token canvas):
-//   gate_up4: workgroup = (tile, 352 output columns); wave w owns pairs 2w and
+// m = 704, gate_up g = 128, down g = 64) runs as one launch of 11-wave
+// workgroups, one per CU, 2 per 32-row tile (256 for the 128 tiles of a
+// 256-token canvas), each for one half h of H's 704 columns:
+//   alignment: each workgroup finds its tile's expert and rows from the
+//     expert ids itself (histogram, fixed-order scan, stable ranks in LDS);
+//   gate_up4: H[:, 352 h .. + 352] of the tile; wave w owns pairs 2w and
 //     2w + 1 (16 gate columns and the matching up columns each) and computes
 //     them in two passes over K (11 line steps of 256 each), straight-line,
 //     with the loads of the second pass issued during the end of the first.
-//     The step's activation slice is staged in LDS once for the 11 waves.
-//   down4: workgroup = (tile, 1408 output columns = 88 weight row tiles); the
-//     tile's activations (all of K = 704) and the block's scales/zero points
-//     are staged in LDS once; wave w streams row tiles w, w + 11, ..., 2 tiles
-//     ahead, storing each tile's fp16 outputs as soon as it is done.
-//   layer4_kernel runs both in one launch: workgroup (tile, half) does gate_up4
-//     for its half of H (gathered in LDS, stored in 16-byte segments),
-//     requests its down scales/zeros and first weight tiles, raises the
-//     tile's counter once its H stores are complete and waits for the
-//     partner half before reading H. This removes the second launch, its
-//     ramp-up and the gate_up tail. H crosses CUs at device scope
-//     (write-through stores, device-scope loads) rather than through
-//     device-scope fences, which would write back and invalidate the whole L2
-//     of an XCD each time. The store acknowledgement still costs one memory
-//     round trip under full load (several microseconds) per workgroup.
-// down4 also runs alone when gate_up has another group size.
+//     The step's activation slice is staged in LDS once for the 11 waves; H
+//     stays in LDS;
+//   down, split along K: the workgroup's H half times the matching half of
+//     every down row gives an fp16 partial of all 2816 outputs, stored per
+//     assignment; the combine adds the two partials. No workgroup waits for
+//     another.
+// down4 (workgroup = (tile, 1408 output columns), the tile's H rows and the
+// block's scales/zero points staged in LDS once, wave w streaming row tiles
+// w, w + 11, ... two ahead) runs as a launch of its own when gate_up has
+// another group size.
 // Other shapes take the generic kernels:
 //   gate_up_kernel: workgroup = (tile, 64 columns), 4 waves, one pair each.
 //   down_kernel: workgroup = (tile, 256 columns), 8 waves, two row tiles each,
@@ -100,15 +96,6 @@ __device__ inline rsrc_t make_rsrc(const void *base, uint32_t bytes)
 __device__ inline uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// The same load at device scope (cache policy sc1): it is served coherently
-// for the whole device, so it sees stores that other CUs made at device scope
-// without any cache invalidation.
-constexpr int kCpolDevice = 16;
-__device__ inline uint4 load16_device(rsrc_t r, uint32_t voff)
-{
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kCpolDevice));
 }
 
 template <int G>
@@ -868,38 +855,29 @@ __attribute__((amdgpu_waves_per_eu(4))) down_kernel(GemmArgs p)
 }
 
 // ===========================================================================
-// Layer-shape kernels (d = 2816, m = 704, gate_up g = 128, down g = 64).
+// Layer-shape kernel (d = 2816, m = 704, gate_up g = 128, down g = 64): the
+// alignment, gate_up with its activation and down in one launch.
 //
 // Activation rows re-read from L2 share each CU's vector-memory path with the
-// weight stream, so these kernels cover wide column blocks per workgroup (the
-// activations are staged once per 352 gate_up columns and once per 1408 down
-// columns) and launch one 11-wave workgroup per CU: 2 per 32-row tile, 256
-// for the 128 tiles of a T = 256 canvas, a single round with one prologue.
-
-// ---- gate_up: workgroup = (tile, 352 output columns); wave w owns pairs 2w
-// and 2w + 1 (columns col0 + 32 w .. + 32) and computes them one after the
-// other: pass 0 walks all of K for pair 2w, pass 1 for pair 2w + 1. The 22
-// line steps run as straight-line code with the loads P steps ahead across
-// the pass boundary; each pass restages the same activation slices.
-// Polls of a counter that another workgroup of the same launch raises; the
-// bound (about 2^16 polls of a microsecond or less) only guarantees that the
-// kernel ends if the counter never gets there.
-constexpr int kSpinLimit = 1 << 16;
-
-// One lane waits until *flag >= target (device-scope loads); the rest of the
-// workgroup follows through a barrier, and the data the counter announces is
-// then read with device-scope loads. A wait that reaches the bound (which a
-// correct launch never does) is counted in *timeouts, so that a caller can
-// tell that the outputs of that call are not to be trusted.
-__device__ __noinline__ void wait_count(const int32_t *flag, int target, int32_t *timeouts)
-{
-    for (int i = 0; i < kSpinLimit; ++i) {
-        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target)
-            return;
-        __builtin_amdgcn_s_sleep(2);
-    }
-    __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// weight stream, so the GEMMs cover wide column blocks per workgroup and the
+// launch runs one 11-wave workgroup per CU: 2 per 32-row tile (one per half
+// h of H's columns), 256 for the 128 tiles of a T = 256 canvas, a single
+// round with one prologue.
+//
+//   1. alignment, per workgroup and sync-free: every workgroup reads all the
+//      expert ids (8 KB at T = 256), builds the expert histogram in LDS,
+//      finds by a fixed-order scan of the 32-padded counts which expert owns
+//      its tile and ranks that expert's ids (ascending flat index) to find
+//      the flat ids of its 32 rows. The result is align_kernel's, with no
+//      launch, no global buffers and no host readback.
+//   2. gate_up: H[:, 352 h .. 352 h + 352] of the tile's rows, kept in LDS.
+//   3. down, split along its contraction: the workgroup multiplies its own
+//      half of H (K = 352 of 704) into all 2816 outputs and stores the fp16
+//      partial at (h, flat id); the combine adds the two halves. No H crosses
+//      CUs and no workgroup waits for another. The split falls inside down's
+//      group 5 (K 320 .. 383): both halves take that group, each with the
+//      lanes that hold the other half's K idle (no load; their activations
+//      are zero in LDS), and each applies the group's scale to its part.
 
 constexpr int kL4Waves = 11;
 constexpr int kL4Threads = kL4Waves * 64;
@@ -911,20 +889,178 @@ constexpr int kGu4Groups = kGuSteps * 2;         // 22 groups of 128
 constexpr int kGu4XRows = kBlockM + 1;          // row 32 takes the writes of rows past the tile
 constexpr int kGu4SzSeg = (kGu4Rows * kGu4Groups * 2 / 16 + kL4Threads - 1) / kL4Threads * kL4Threads;
 
-constexpr int kGu4HSeg = kGu4Cols * 2 / 16;      // 16-byte segments of one H row half (44)
+// The H tile in LDS: 32 rows of the half's 352 columns placed at column
+// 32 h of a 384-column frame (the other 32 columns zero), so that local
+// down group j (global group j + 5 h) reads its 64 K at column 64 j for
+// either half; rows padded by 16 bytes against bank conflicts.
+constexpr int kHCols = 384;
+constexpr int kHPitch = kHCols + 8;              // fp16 per LDS row
 
-constexpr size_t gate_up4_lds_bytes()
+constexpr size_t layer_gate_up_lds_bytes()
 {
-    return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg +
-           sizeof(uint4) * kBlockM * kGu4HSeg;
+    return sizeof(uint4) * 2 * kGu4XRows * kStepPitch + 2 * sizeof(uint4) * kGu4SzSeg;
 }
 
-// H is gathered in LDS and stored at device scope (written through to
-// memory) in whole 16-byte segments: its consumer is the down half of the
-// same launch, on another CU.
-template <int NMS, bool TL, bool NT>
-__device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int valid, int row0, int cb,
-                                              const int (&fidr)[2])
+constexpr size_t layer_lds_bytes()
+{
+    return layer_gate_up_lds_bytes() + sizeof(uint16_t) * kBlockM * kHPitch;
+}
+
+// ---- 1. alignment inside the kernel, in two parts: which expert owns the
+// tile (a histogram of all ids, then a fixed-order scan of the 32-padded
+// counts), and, once its weight loads are in flight, the flat ids of its
+// rows (stable ranks of that expert's ids).
+
+constexpr int kSetupPer = 4;                     // ids per thread per chunk
+constexpr int kSetupChunk = kL4Threads * kSetupPer;
+
+// Exclusive scan of v over the workgroup's threads in thread order (a fixed
+// order); *total gets the sum. Every thread must call it.
+__device__ inline int l4_scan_excl(int v, int *s_wsum, int &total)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(x, off, 64);
+        if (lane >= off)
+            x += u;
+    }
+    if (lane == 63)
+        s_wsum[wave] = x;
+    __syncthreads();
+    int base = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kL4Waves; ++w) {
+        const int s = s_wsum[w];
+        base += w < wave ? s : 0;
+        total += s;
+    }
+    __syncthreads();                              // s_wsum is reused by the next scan
+    return base + x - v;
+}
+
+struct TileSetup {
+    int v0[kSetupPer];                            // this thread's ids of the first chunk
+    int r0;                                       // the tile's first row within its expert
+    int valid;                                    // rows holding assignments
+    int tiles;                                    // tiles of the expert
+};
+
+__device__ inline void load_ids(const int32_t *__restrict__ ids, int A, int c0, int (&v)[kSetupPer])
+{
+#pragma unroll
+    for (int j = 0; j < kSetupPer; ++j) {
+        const int i = c0 + (int)threadIdx.x * kSetupPer + j;
+        v[j] = i < A ? ids[i] : -1;
+    }
+}
+
+// The tile's expert, or -1 when the tile lies past the padded total. Ids
+// outside [0, E) are skipped. Also sets every s_rows entry to A (pad).
+__device__ int layer_tile_find(const int32_t *__restrict__ ids, int A, int E, int tile, TileSetup &ts,
+                               int *s_cnt, int *s_wsum, int *s_rows, int *s_info)
+{
+    const int tid = threadIdx.x;
+    for (int x = tid; x < E; x += kL4Threads)
+        s_cnt[x] = 0;
+    if (tid < kBlockM)
+        s_rows[tid] = A;
+    if (tid == 0)
+        s_info[0] = -1;
+    load_ids(ids, A, 0, ts.v0);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kSetupPer; ++j)
+        if (ts.v0[j] >= 0 && ts.v0[j] < E)
+            atomicAdd(&s_cnt[ts.v0[j]], 1);
+    for (int c0 = kSetupChunk; c0 < A; c0 += kSetupChunk) {
+        int v[kSetupPer];
+        load_ids(ids, A, c0, v);
+#pragma unroll
+        for (int j = 0; j < kSetupPer; ++j)
+            if (v[j] >= 0 && v[j] < E)
+                atomicAdd(&s_cnt[v[j]], 1);
+    }
+    __syncthreads();
+    // padded offsets in expert order; the expert whose rows hold the tile's first
+    const int row = tile * kBlockM;
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += kL4Threads) {
+        const int e = e0 + tid;
+        const int cnt = e < E ? s_cnt[e] : 0;
+        const int padded = (cnt + kBlockM - 1) / kBlockM * kBlockM;
+        int total;
+        const int off = base + l4_scan_excl(padded, s_wsum, total);
+        if (e < E && off <= row && row < off + padded) {
+            s_info[0] = e;
+            s_info[1] = off;
+            s_info[2] = cnt;
+            s_info[3] = padded / kBlockM;
+        }
+        base += total;
+    }
+    __syncthreads();
+    // uniform over the workgroup: scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
+    if (e >= 0) {
+        ts.r0 = __builtin_amdgcn_readfirstlane(row - s_info[1]);
+        ts.valid = __builtin_amdgcn_readfirstlane(min(kBlockM, s_info[2] - ts.r0));
+        ts.tiles = __builtin_amdgcn_readfirstlane(s_info[3]);
+    }
+    return e;
+}
+
+// s_rows[r] = the flat id of the tile's row r: the (r0 + r)-th of expert e's
+// ids in ascending flat index. Thread t holds ids c0 + 4 t .. c0 + 4 t + 3
+// of each chunk, so thread order is index order.
+__device__ void layer_tile_rows(const int32_t *__restrict__ ids, int A, int e, const TileSetup &ts,
+                                int *s_wsum, int *s_rows)
+{
+    const int tid = threadIdx.x;
+    int run = 0;
+    for (int c0 = 0; c0 < A && run < ts.r0 + kBlockM; c0 += kSetupChunk) {
+        int v[kSetupPer];
+        if (c0 == 0) {
+#pragma unroll
+            for (int j = 0; j < kSetupPer; ++j)
+                v[j] = ts.v0[j];
+        } else {
+            load_ids(ids, A, c0, v);
+        }
+        int mine = 0;
+#pragma unroll
+        for (int j = 0; j < kSetupPer; ++j)
+            mine += v[j] == e;
+        int total;
+        int rank = run + l4_scan_excl(mine, s_wsum, total);
+#pragma unroll
+        for (int j = 0; j < kSetupPer; ++j) {
+            if (v[j] == e) {
+                const int r = rank - ts.r0;
+                if (r >= 0 && r < kBlockM)
+                    s_rows[r] = c0 + tid * kSetupPer + j;
+                ++rank;
+            }
+        }
+        run += total;
+    }
+    __syncthreads();
+}
+
+// ---- 2. gate_up: workgroup = (tile, 352 output columns); wave w owns pairs
+// 2w and 2w + 1 (columns col0 + 32 w .. + 32) and computes them one after the
+// other: pass 0 walks all of K for pair 2w, pass 1 for pair 2w + 1. The 22
+// line steps run as straight-line code with the loads P steps ahead across
+// the pass boundary; each pass restages the same activation slices.
+// H = gelu_tanh(gate) * up goes to the LDS frame (see kHPitch). rows fills
+// the flat ids of the activation rows once the first weight loads are out;
+// after_k runs once the last step's weights are consumed, before the last
+// epilogue: the down phase issues its first loads there.
+template <int NMS, bool TL, bool NT, class Rows, class AfterK>
+__device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, Rows &&rows,
+                                              AfterK &&after_k)
 {
     constexpr int G = 128;
     constexpr int P = kGu4Ahead;
@@ -948,11 +1084,11 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
     uint4 *lds_x = lds;                                             // [2][33][kStepPitch]
     uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kGu4XRows * kStepPitch);   // [704 rows][NG]
     uint16_t *lds_z = lds_s + kGu4SzSeg * 8;
-    uint16_t *lds_h = lds_z + kGu4SzSeg * 8;                       // [32 rows][352] H, permuted per 8
+    uint16_t *lds_h = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(lds) + layer_gate_up_lds_bytes());
 
     // ---- 1. scale/zero of the 352 gate and 352 up rows, then per step the
-    // activations and the weights (in issue order: row ids, scale/zero,
-    // then step by step)
+    // activations and the weights (in issue order: scale/zero, then step by
+    // step)
     const uint32_t sz_bytes = (uint32_t)p.n_w * (uint32_t)NG * 2u;
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, sz_bytes);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, sz_bytes);
@@ -987,6 +1123,14 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
                 bq[st][u][h] = load_frag<G, NT>(rq, voff, wq_group_off<G, TL>(s * SG + h));
         }
     };
+    // the weights of the first steps go out before the tile's rows are known
+    issue_w(0, 0);
+#pragma unroll
+    for (int q = 1; q < P; ++q)
+        issue_w(q, q);
+    __builtin_amdgcn_sched_barrier(0);
+    int fidr[2];
+    rows(fidr);
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
     const int xseg = tid % kStepSeg;
     uint32_t xoff[XLD];
@@ -1004,16 +1148,12 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
         for (int i = 0; i < XLD; ++i)
             xr[st][i] = load16(ra, xoff[i] != kOutOfRange ? xoff[i] + (uint32_t)s * 512u : kOutOfRange, 0);
     };
-    // prologue: x(0) w(0) x(1) w(1) w(2); in step q: x(q + PX) then w(q + P),
-    // so waiting for a step's activations never waits for later weights
-    issue_x(0, 0);
-    issue_w(0, 0);
+    // prologue: w(0) w(1) w(2) (above), x(0) x(1); in step q: x(q + PX) then
+    // w(q + P), so waiting for a step's activations never waits for later
+    // weights
 #pragma unroll
-    for (int q = 1; q < P; ++q) {
-        if (q < PX)
-            issue_x(q, q);
-        issue_w(q, q);
-    }
+    for (int q = 0; q < PX; ++q)
+        issue_x(q, q);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. scale/zero into LDS (made visible by the first step's barrier;
@@ -1100,40 +1240,249 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int vali
             if (q + P < NQ)
                 issue_w(st, q + P);
         }
+        if (c == 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            after_k();
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // epilogue of the pass: H = gelu_tanh(gate) * up in fp16, permuted per
-        // 8, into the LDS tile (each wave owns its columns)
-        const int hcol = permuted_col(in_range(c));       // col0 is a multiple of 8
+        // 8, into the LDS frame at column 32 cb + local column (each wave owns
+        // its columns); rows past the tile's valid rows hold gelu(0) * 0 = 0
+        const int hcol = kBlockM * cb + permuted_col(in_range(c));   // 32 cb is a multiple of 8
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = ms * 16 + quarter * 4 + i;
                 const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
-                lds_h[r * kGu4Cols + hcol] = __builtin_bit_cast(uint16_t, (_Float16)h);
+                lds_h[r * kHPitch + hcol] = __builtin_bit_cast(uint16_t, (_Float16)h);
             }
         }
     }
-
-    // ---- 4. the valid rows of the H tile to memory, 16 bytes per store
-    __syncthreads();
-    const rsrc_t rh = make_rsrc(p.out, (uint32_t)(p.max_tiles * kBlockM) * (uint32_t)n_out * 2u);
-    const uint4 *lh = reinterpret_cast<const uint4 *>(lds_h);
-    constexpr int kHStores = (kBlockM * kGu4HSeg + kL4Threads - 1) / kL4Threads;   // 2
-#pragma unroll
-    for (int i = 0; i < kHStores; ++i) {
-        const int x = i * kL4Threads + tid;
-        const int r = x / kGu4HSeg, sg = x - r * kGu4HSeg;
-        const uint32_t off = r < valid ? (uint32_t)(row0 + r) * (uint32_t)n_out * 2u + (uint32_t)col0 * 2u +
-                                             (uint32_t)sg * 16u
-                                       : kOutOfRange;
-        const uint4 v = lh[min(x, kBlockM * kGu4HSeg - 1)];
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rh, off, 0, kCpolDevice);
+    // the frame's 32 columns outside this half: zero (rows 16 NMS .. 31 are
+    // never read)
+    if (tid < kBlockM * 4) {
+        const int r = tid >> 2, sg = tid & 3;
+        const int col = (cb == 0 ? kGu4Cols : 0) + sg * 8;
+        *reinterpret_cast<uint4 *>(lds_h + r * kHPitch + col) = make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
-// ---- down: workgroup = (tile, 1408 output columns = 88 row tiles); wave w
-// streams row tiles w, w + 11, ..., w + 77 (the 11 waves read neighbouring
-// tiles at any time), P tiles ahead, each tile's output stored when done.
+// ---- 3. down, the workgroup's half of the contraction into all outputs.
+// Wave w streams row tiles w, w + 11, ..., w + 165 (16 of the 176 row tiles of
+// d = 2816), P tiles ahead; a tile covers the half's 6 local groups (global
+// groups 5 h .. 5 h + 5). With each tile's weights the wave loads the tile's
+// 16 rows of scales and zero points (352 contiguous bytes each: lanes 0-21
+// and 22-43 take 16 bytes apiece) and lays them out in a slot of LDS of its
+// own, from which its lanes read what they need: no workgroup-wide staging
+// and no barrier. The MFMA takes the weights as its row operand, so a lane
+// ends with four consecutive output columns of one assignment row and
+// stores them (8 bytes of the fp16 partial) as soon as the tile is done.
+constexpr int kKsTiles = 16;                     // row tiles per wave
+constexpr int kKsGroups = 6;                     // local groups per half
+constexpr int kKsAhead = 3;                      // row tiles in flight per wave
+constexpr int kKsSzLanes = 16 * kDnGroups * 2 / 16;   // 22 lanes of 16 bytes per array
+constexpr int kKsSlot = 2 * 16 * kDnGroups * 2;  // bytes of one tile's scales + zeros (704)
+
+static_assert(kL4Waves * kKsAhead * kKsSlot <= layer_gate_up_lds_bytes(),
+              "the waves' scale/zero slots fit where gate_up's staging was");
+
+struct DownKsPrefetch {
+    Frag<64> bq[kKsAhead][kKsGroups];            // weights of the row tiles in flight
+    uint4 sz[kKsAhead];                          // the lane's 16 bytes of their scales/zeros
+};
+
+// Lanes of local group j that hold K of the other half: quarters 2, 3 of
+// group 5 for h = 0, quarters 0, 1 of group 5 for h = 1.
+__device__ inline bool ks_idle(int h, int j, int quarter)
+{
+    return h == 0 ? (j == kKsGroups - 1 && quarter >= 2) : (j == 0 && quarter < 2);
+}
+
+// Loads of row tile j (of this wave) into prefetch stage st.
+template <bool TL, bool NT>
+__device__ __forceinline__ void down_ks_issue(const GemmArgs &p, int e, int h, int wave, int lane,
+                                              DownKsPrefetch &pf, int st, int j)
+{
+    constexpr int K = kDnGroups * 64;
+    constexpr int NG = kDnGroups;
+    const size_t wexp = (size_t)e * p.n_w;
+    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
+    const int quarter = lane >> 4;
+    const int rt = wave + j * kL4Waves;           // row tile
+    const uint32_t voff = j < kKsTiles ? wq_lane_off<64, TL>(rt * 16 + (lane & 15), lane, K) : kOutOfRange;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g)
+        pf.bq[st][g] = load_frag<64, NT>(rq, ks_idle(h, g, quarter) ? kOutOfRange : voff,
+                                         wq_group_off<64, TL>(g + 5 * h));
+    if (j < kKsTiles && lane < 2 * kKsSzLanes) {
+        const uint16_t *src = (lane < kKsSzLanes ? p.s : p.z) + wexp * NG + (size_t)rt * 16 * NG;
+        pf.sz[st] = *reinterpret_cast<const uint4 *>(src + (lane % kKsSzLanes) * 8);
+    }
+}
+
+template <bool TL, bool NT>
+__device__ __forceinline__ void down_ks_prefetch(const GemmArgs &p, int e, int h, DownKsPrefetch &pf)
+{
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+    for (int j = 0; j < kKsAhead; ++j)
+        down_ks_issue<TL, NT>(p, e, h, wave, tid & 63, pf, j, j);
+}
+
+template <int NMS, bool TL, bool NT>
+__device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, const int *s_rows,
+                                             int valid, DownKsPrefetch &pf)
+{
+    constexpr int G = 64;
+    constexpr int P = kKsAhead;
+    constexpr int NG = kDnGroups;
+    constexpr int kWords = 2;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lrow = lane & 15;
+    const int quarter = lane >> 4;
+    const int n_out = p.n_out;
+
+    extern __shared__ uint4 lds[];
+    char *slots = reinterpret_cast<char *>(lds) + wave * P * kKsSlot;   // this wave's, over gate_up's staging
+    const uint16_t *lds_h = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(lds) +
+                                                               layer_gate_up_lds_bytes());
+    // H complete; every wave is done with gate_up's staging
+    __syncthreads();
+    int dst[NMS];                                  // output rows (flat ids) of this lane's MFMA rows
+#pragma unroll
+    for (int ms = 0; ms < NMS; ++ms)
+        dst[ms] = ms * 16 + lrow < valid ? s_rows[ms * 16 + lrow] : -1;
+
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    uint16_t *Y = static_cast<uint16_t *>(p.out) + (size_t)h * (size_t)p.A * (size_t)n_out;
+#pragma unroll
+    for (int j = 0; j < kKsTiles; ++j) {
+        const int st = j % P;
+        // the tile's scales [16][11] then zero points [16][11] into the slot;
+        // the same wave reads them back (its LDS operations run in order)
+        char *slot = slots + st * kKsSlot;
+        if (lane < 2 * kKsSzLanes)
+            *reinterpret_cast<uint4 *>(slot + lane * 16) = pf.sz[st];
+        const uint16_t *ls = reinterpret_cast<const uint16_t *>(slot);
+        const uint16_t *lz = ls + 16 * NG;
+        int aoff = 0;                              // keeps the H reads per tile (see gate_up)
+        asm volatile("" : "+v"(aoff));
+        const int srow = (wave + j * kL4Waves) * 16;   // first weight row (output column)
+        f32x4 out[NMS];
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            out[ms] = zero4;
+#pragma unroll
+        for (int g = 0; g < kKsGroups; ++g) {
+            asm volatile("" : "+v"(aoff));         // and per group: no hoisting of later groups' reads
+            const int gg = g + 5 * h;              // global group
+            f16x2 c1024, c64;
+            zero_point_consts(lz[lrow * NG + gg], c1024, c64);
+            float sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[i] = (float)__builtin_bit_cast(_Float16, ls[(quarter * 4 + i) * NG + gg]);
+            f32x4 prt[NMS];
+#pragma unroll
+            for (int t = 0; t < kWords; ++t) {
+                const f16x8 bop = dequant8(frag_word<G>(pf.bq[st][g], t), c1024, c64);
+                const int col = g * G + quarter * (G / 4) + t * 8;   // K in the frame
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+                    const f16x8 aop = *reinterpret_cast<const f16x8 *>(
+                        lds_h + aoff + (ms * 16 + lrow) * kHPitch + col);
+                    prt[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop, aop, t == 0 ? zero4 : prt[ms], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    out[ms][i] += sc[i] * prt[ms][i];
+                asm volatile("" : "+v"(out[ms]));   // pin the accumulation (see gate_up)
+            }
+        }
+        down_ks_issue<TL, NT>(p, e, h, wave, lane, pf, st, j + P);
+        const int col = srow + quarter * 4;
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            if (dst[ms] >= 0)
+                *reinterpret_cast<uint2 *>(Y + (size_t)dst[ms] * n_out + col) = pack_f16x4(out[ms]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Rows: a callable that ranks the tile's rows into s_rows and fills fidr
+// (the activation rows' flat ids for gate_up's staging), run once the first
+// weight loads are out.
+template <int NMS, bool TL, bool NT, class Rows>
+__device__ __forceinline__ void layer_body(const GemmArgs &gu, const GemmArgs &dn, int e, int h,
+                                           Rows &&rows, const int *s_rows, int valid)
+{
+    DownKsPrefetch pf;
+    gate_up4_body<NMS, TL, NT>(gu, e, h, rows, [&]() { down_ks_prefetch<TL, NT>(dn, e, h, pf); });
+    down_ks_body<NMS, TL, NT>(dn, e, h, s_rows, valid, pf);
+}
+
+// Workgroup -> (half, tile), both halves of a tile on one XCD (consecutive
+// workgroups go to the 8 XCDs in turn), so a tile's activation rows stay in
+// one L2. Y gets the two fp16 partials [2][A][d] at each assignment's flat id.
+template <bool TL>
+__global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs dn,
+                                                           const int32_t *__restrict__ ids, int E)
+{
+    __shared__ int s_cnt[kMaxExperts];
+    __shared__ int s_wsum[kL4Waves];
+    __shared__ int s_rows[kBlockM];
+    __shared__ int s_info[4];
+    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
+    const int h = slot % 2;
+    const int tile = slot / 2 * kXcds + xcd;
+    if (tile >= gu.max_tiles)
+        return;
+    TileSetup ts;
+    const int e = layer_tile_find(ids, gu.A, E, tile, ts, s_cnt, s_wsum, s_rows, s_info);
+    if (e < 0)
+        return;
+    auto rows = [&](int (&fidr)[2]) {
+        layer_tile_rows(ids, gu.A, e, ts, s_wsum, s_rows);
+        const int tid = threadIdx.x;
+        fidr[0] = s_rows[tid / kStepSeg];
+        fidr[1] = s_rows[min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];
+    };
+    const int valid = ts.valid;
+    // tiled weights of an expert that no other tile reads stream past the
+    // caches; those of an expert with several tiles stay cacheable
+    const bool nt = TL && ts.tiles == 1;
+    // (the distinct asm statements keep the compiler from hoisting the arms'
+    // common prologue above the branch, which spills)
+    if (valid > 16) {
+        if (nt) {
+            asm volatile("; streaming weights");
+            layer_body<2, TL, TL>(gu, dn, e, h, rows, s_rows, valid);
+        } else {
+            asm volatile("; cached weights");
+            layer_body<2, TL, false>(gu, dn, e, h, rows, s_rows, valid);
+        }
+    } else {
+        if (nt) {
+            asm volatile("; streaming weights");
+            layer_body<1, TL, TL>(gu, dn, e, h, rows, s_rows, valid);
+        } else {
+            asm volatile("; cached weights");
+            layer_body<1, TL, false>(gu, dn, e, h, rows, s_rows, valid);
+        }
+    }
+}
+
+// ---- down alone (gate_up at another group size): workgroup = (tile, 1408
+// output columns = 88 row tiles); wave w streams row tiles w, w + 11, ...,
+// w + 77, P tiles ahead, each tile's output stored when done; H from the
+// gate_up launch, the tile's rows from the alignment kernel.
 constexpr int kDn4Tiles = 8;                     // row tiles per wave
 constexpr int kDn4Rows = kL4Waves * kDn4Tiles * 16;   // 1408 weight rows per workgroup
 constexpr int kDn4Ahead = 2;
@@ -1144,22 +1493,9 @@ constexpr size_t down4_lds_bytes()
     return sizeof(uint4) * kBlockM * (kDnGroups * 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * kDnGroups;
 }
 
-// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
-// memory operations are outstanding and leaves the other counters alone
-constexpr int vmcnt_at_most(int n)
-{
-    return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
-}
-
-// FUSED: this workgroup has just issued its half of H (device-scope stores)
-// in the same launch. The scale/zero and first weight loads go out first;
-// then, once only those loads can still be outstanding, the stores are
-// complete and the half is announced; av is loaded once the counter shows
-// both halves.
-template <int NMS, bool FUSED, bool TL, bool NT>
+template <int NMS, bool TL, bool NT>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
-                                           uint4 (&av)[kDn4ALoads], int fid, int32_t *ready,
-                                           int32_t *ready_end)
+                                           const uint4 (&av)[kDn4ALoads], int fid)
 {
     constexpr int G = 64;
     constexpr int P = kDn4Ahead;
@@ -1210,18 +1546,6 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     for (int j = 0; j < P; ++j)
         issue_w(j, j);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (FUSED) {
-        // vector memory operations issued since the H stores: scale/zero, weights
-        constexpr int kIssued = 2 * kSzLoads + P * NG;
-        static_assert(kIssued < 64, "vmcnt range");
-        __builtin_amdgcn_s_waitcnt(vmcnt_at_most(kIssued));
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();                           // also: every wave is done with gate_up's LDS
-        if (tid == 0) {
-            __hip_atomic_fetch_add(ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            wait_count(ready, 2, ready_end);
-        }
-    }
 
     // ---- 2. scale/zero (transposed to [g][row]), activations and row
     // destinations into LDS
@@ -1243,13 +1567,6 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
                 put8(lds_z, x, zv[i]);
             }
         }
-    }
-    if constexpr (FUSED) {
-        __syncthreads();                           // lane 0 has seen both halves
-        const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
-#pragma unroll
-        for (int i = 0; i < kDn4ALoads; ++i)
-            av[i] = load16_device(ra, down_a_off(p, row0, i * kL4Threads + tid));
     }
 #pragma unroll
     for (int i = 0; i < kDn4ALoads; ++i) {
@@ -1347,88 +1664,14 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     const bool more = tile_valid(info.y) > 16;
     if (TL && tile_count(info.y) == 1) {
         if (more)
-            down4_body<2, false, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+            down4_body<2, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
         else
-            down4_body<1, false, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+            down4_body<1, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
     } else {
         if (more)
-            down4_body<2, false, TL, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
+            down4_body<2, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
         else
-            down4_body<1, false, TL, false>(p, info.x, tile * kBlockM, cb, av, fid, nullptr, nullptr);
-    }
-}
-
-// ---- gate_up and down of the layer's shape in one launch. Workgroup (tile,
-// column half) runs gate_up4 for its half of H, announces it on the tile's
-// counter, then runs down4 for its half of the outputs once both halves of H
-// are there. The two halves of a tile are neighbours in dispatch order on
-// one XCD, so a workgroup only ever waits for a partner that is resident or
-// next in line, and H stays in that XCD's L2. The counters start at zero
-// (the alignment step clears them) and the wait is bounded; ready[max_tiles]
-// counts waits that hit the bound.
-constexpr size_t layer4_lds_bytes()
-{
-    return gate_up4_lds_bytes() > down4_lds_bytes() ? gate_up4_lds_bytes() : down4_lds_bytes();
-}
-
-template <bool TL>
-__global__ void __launch_bounds__(kL4Threads) layer4_kernel(GemmArgs gu, GemmArgs dn, int32_t *ready)
-{
-    const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
-    const int cb = slot % 2;
-    const int tile = slot / 2 * kXcds + xcd;
-    if (tile >= gu.max_tiles)
-        return;
-    const int tid = threadIdx.x;
-    int fidr[2];
-    fidr[0] = gu.sorted_ids[tile * kBlockM + tid / kStepSeg];
-    fidr[1] = gu.sorted_ids[tile * kBlockM + min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];
-    int fid = dn.A;                                // down's row destination, for later
-    if (tid < kBlockM)
-        fid = dn.sorted_ids[tile * kBlockM + tid];
-    const int2 info = gu.tile_info[tile];
-    if (info.x < 0)
-        return;
-    const int valid = tile_valid(info.y);
-    // tiled weights of an expert that no other tile reads stream past the
-    // caches; those of an expert with several tiles stay cacheable
-    const bool nt = TL && tile_count(info.y) == 1;
-    // (the distinct asm statements keep the compiler from hoisting the two
-    // gate_up arms' common prologue above the branch, which spills)
-    if (valid > 16) {
-        if (nt) {
-            asm volatile("; streaming weights");
-            gate_up4_body<2, TL, TL>(gu, info.x, valid, tile * kBlockM, cb, fidr);
-        } else {
-            asm volatile("; cached weights");
-            gate_up4_body<2, TL, false>(gu, info.x, valid, tile * kBlockM, cb, fidr);
-        }
-    } else {
-        if (nt) {
-            asm volatile("; streaming weights");
-            gate_up4_body<1, TL, TL>(gu, info.x, valid, tile * kBlockM, cb, fidr);
-        } else {
-            asm volatile("; cached weights");
-            gate_up4_body<1, TL, false>(gu, info.x, valid, tile * kBlockM, cb, fidr);
-        }
-    }
-    // nothing but the down body's own loads may follow the H stores before
-    // it announces the half (it counts them); device-scope fences are not
-    // used for that: they would write back and invalidate the whole L2 of
-    // the XCD, stalling every other workgroup streaming through it
-    __builtin_amdgcn_sched_barrier(0);
-    uint4 av[kDn4ALoads];
-    int32_t *const timeouts = ready + gu.max_tiles;
-    if (valid > 16) {
-        if (nt)
-            down4_body<2, true, TL, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
-        else
-            down4_body<2, true, TL, false>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
-    } else {
-        if (nt)
-            down4_body<1, true, TL, TL>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
-        else
-            down4_body<1, true, TL, false>(dn, info.x, tile * kBlockM, cb, av, fid, ready + tile, timeouts);
+            down4_body<1, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
     }
 }
 
@@ -1468,14 +1711,15 @@ hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
 }
 
 template <bool TL>
-hipError_t launch_layer4(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready, hipStream_t stream)
+hipError_t launch_layer_k(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,
+                          hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;
-    hipError_t err = allow_lds(layer4_kernel<TL>, layer4_lds_bytes(), allowed);
+    hipError_t err = allow_lds(layer_kernel<TL>, layer_lds_bytes(), allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (gu.max_tiles + kXcds - 1) / kXcds * kXcds;
-    layer4_kernel<TL><<<dim3(tiles * 2), dim3(kL4Threads), layer4_lds_bytes(), stream>>>(gu, dn, ready);
+    layer_kernel<TL><<<dim3(tiles * 2), dim3(kL4Threads), layer_lds_bytes(), stream>>>(gu, dn, ids, E);
     return hipGetLastError();
 }
 
@@ -1572,19 +1816,21 @@ hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
     return g == 128 ? launch_linear_g<128, false>(a, stream) : launch_linear_g<64, false>(a, stream);
 }
 
-bool gate_up_down_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g)
+bool layer_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g, int E)
 {
-    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g) && gu.tiled == dn.tiled;
+    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g) && gu.tiled == dn.tiled &&
+           E <= kMaxExperts;
 }
 
-hipError_t launch_gate_up_down(const GemmArgs &gu, const GemmArgs &dn, int32_t *ready,
-                               hipStream_t stream)
+hipError_t launch_layer(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,
+                        hipStream_t stream)
 {
     if (gu.max_tiles == 0)
         return hipSuccess;
     if (gu.tiled != dn.tiled)
-        return hipErrorInvalidValue;               // gate_up_down_fused() is false for a mixed pair
-    return gu.tiled ? launch_layer4<true>(gu, dn, ready, stream) : launch_layer4<false>(gu, dn, ready, stream);
+        return hipErrorInvalidValue;               // layer_fused() is false for a mixed pair
+    return gu.tiled ? launch_layer_k<true>(gu, dn, ids, E, stream)
+                    : launch_layer_k<false>(gu, dn, ids, E, stream);
 }
 
 }  // namespace dgw4
