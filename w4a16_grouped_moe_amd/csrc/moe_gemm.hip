@@ -1339,7 +1339,8 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
     constexpr int P = kKsAhead;
     constexpr int NG = kDnGroups;
     constexpr int kWords = 2;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));                  // recomputed here, not kept from gate_up
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 15;
