@@ -290,6 +290,26 @@ DGW4_API int dgw4_sample(const float *logits, int R, int V, uint64_t seed, float
                          void *stream);
 
 /*
+ * dgw4_sample_noalloc — dgw4_sample for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same kernels and results, with the partials in a
+ * fixed 1 MiB array that the library holds on each device for the life of
+ * the process instead of a caller workspace. It allocates nothing. Shapes
+ * whose partials need more (sample_workspace_bytes > 1 MiB: R x splits x 32
+ * bytes, which holds for any V up to R = 32768 rows) return
+ * DGW4_ERR_UNSUPPORTED before anything is launched; other checks as for
+ * dgw4_sample. The array belongs to the device that is current when the call
+ * is made, and `stream` must belong to that device. Every call on a device
+ * shares its array: calls that overlap on one device (other streams, other
+ * host threads) race and must be serialised by the caller; calls in order on
+ * one stream are fine. Nothing in the array needs to start at zero (each
+ * partial is written before it is read).
+ */
+DGW4_API int dgw4_sample_noalloc(const float *logits, int R, int V, uint64_t seed,
+                                 float *entropy, int32_t *sample, int32_t *argmax,
+                                 void *stream);
+
+/*
  * dgw4_hbm_read_probe — a measurement aid, not a step of the layer: reads
  * `bytes` bytes of device memory at `buf` once, with the whole chip
  * (16-byte non-temporal loads, several in flight per lane), so that the elapsed time on

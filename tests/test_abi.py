@@ -187,3 +187,17 @@ def test_layout_flag_bits():
     p = 1 << 12
     assert f(p, 4, 256, 64, p, p, p, 64 | 0x40000, p, None) == B.ERR_INVALID_ARG
     assert f(None, 0, 256, 64, None, None, None, 64 | tiled, None, None) == B.OK
+
+
+def test_sample_noalloc_rejects():
+    f = dg.lib().dgw4_sample_noalloc
+    p = 1 << 12
+    # partials past the fixed 1 MiB array, checked before any HIP call
+    assert f(p, 40000, 4, 0, None, None, p, None) == B.ERR_UNSUPPORTED
+    assert f(p, 4, 6, 0, None, None, p, None) == B.ERR_UNSUPPORTED          # V % 4
+    assert f(p, -1, 1024, 0, None, None, p, None) == B.ERR_INVALID_ARG
+    assert f(p, 4, 2, 0, None, None, p, None) == B.ERR_INVALID_ARG          # V < 4
+    assert f(None, 0, 1024, 0, None, None, None, None) == B.OK               # R = 0
+    assert f(None, 4, 1024, 0, None, None, p, None) == B.ERR_INVALID_ARG     # null logits
+    assert f(p + 4, 4, 1024, 0, None, None, p, None) == B.ERR_INVALID_ARG    # misaligned
+

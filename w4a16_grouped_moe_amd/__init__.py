@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     workspace_bytes,
     w4a16_linear,
     sample,
+    sample_noalloc,
     fused_entropy,
     moe_experts,
     gumbel_argmax_sample,

@@ -70,6 +70,8 @@ def lib():
                                        P, ctypes.POINTER(S), P]
         L.dgw4_sample.restype = I
         L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
+        L.dgw4_sample_noalloc.restype = I
+        L.dgw4_sample_noalloc.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P]
         L.dgw4_pack_tiled.restype = I
         L.dgw4_pack_tiled.argtypes = [P, I, I, I, I, P, P]
         L.dgw4_hbm_read_probe.restype = I
@@ -208,6 +210,28 @@ def sample(logits: torch.Tensor, seed: int = 0, entropy: bool = True, draw: bool
         smp.data_ptr() if smp is not None else None, am.data_ptr(), pws, ctypes.byref(n),
         _stream(logits)))
     return h, smp, am
+
+
+def sample_noalloc(logits: torch.Tensor, seed: int = 0, out=None):
+    """sample() through dgw4_sample_noalloc: the library's own partials, no
+    workspace. ``out`` = (entropy fp32 [R] or None, sample int32 [R] or
+    None, argmax int32 [R]) preallocated by the caller; returns it."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    pl = _dev(logits, "logits", (torch.float32,))
+    if out is None:
+        dev = logits.device
+        out = (torch.empty(R, dtype=torch.float32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev))
+    h, smp, am = out
+    ptrs = [_dev(t, n, d).__int__() if t is not None else None
+            for t, n, d in ((h, "entropy", (torch.float32,)), (smp, "sample", (torch.int32,)),
+                            (am, "argmax", (torch.int32,)))]
+    _check("dgw4_sample_noalloc", lib().dgw4_sample_noalloc(
+        pl, R, V, int(seed) & (2**64 - 1), ptrs[0], ptrs[1], ptrs[2], _stream(logits)))
+    return out
 
 
 def fused_entropy(logits: torch.Tensor) -> torch.Tensor:

@@ -312,6 +312,27 @@ int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T, int topk
                             false);
 }
 
+int dgw4_sample_noalloc(const float *logits, int R, int V, uint64_t seed, float *entropy,
+                        int32_t *sample, int32_t *argmax, void *stream)
+{
+    if (R < 0 || V < 4)
+        return DGW4_ERR_INVALID_ARG;
+    if (V % 4 != 0 || (long long)R * V >= (1LL << 40) || V >= (1 << 30))
+        return DGW4_ERR_UNSUPPORTED;
+    if (dgw4::sample_workspace_bytes(R, V) > dgw4::kSampleScratchBytes)
+        return DGW4_ERR_UNSUPPORTED;
+    if (R == 0)
+        return DGW4_OK;
+    if (!logits || !aligned(logits, 16))
+        return DGW4_ERR_INVALID_ARG;
+    void *part = nullptr;
+    hipError_t err = dgw4::sample_scratch(&part);
+    if (err != hipSuccess)
+        return from_hip(err);
+    return from_hip(dgw4::launch_sample(logits, R, V, seed, entropy, sample, argmax, part,
+                                        (hipStream_t)stream));
+}
+
 int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream)
 {
     if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16))

@@ -91,6 +91,12 @@ size_t sample_workspace_bytes(int R, int V);
 hipError_t launch_sample(const float *logits, int R, int V, uint64_t seed, float *entropy,
                          int32_t *sample, int32_t *argmax, void *workspace, hipStream_t stream);
 
+// The sampler's own partials for callers that cannot allocate: a static
+// device array of kSampleScratchBytes per device; sample_scratch gives its
+// address on the current device (looked up once per device).
+constexpr size_t kSampleScratchBytes = size_t(1) << 20;
+hipError_t sample_scratch(void **ptr);
+
 // One read of `bytes` (a multiple of 16) at buf over the whole chip; see
 // dgw4_hbm_read_probe.
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);

@@ -24,6 +24,7 @@
 #include "dgw4_internal.hpp"
 
 #include <climits>
+#include <mutex>
 
 namespace dgw4 {
 namespace {
@@ -232,6 +233,38 @@ __global__ void __launch_bounds__(64) sample_merge_kernel(const Partial *__restr
 }
 
 }  // namespace
+
+// Partials of dgw4_sample_noalloc: a fixed array that every device the
+// library runs on holds for the life of the process. In host code its name
+// only stands for the symbol; its device address is looked up once per
+// device (sample_scratch) and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[kSampleScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch[kMaxDevices];                      // per device, set on first use
+}  // namespace
+
+hipError_t sample_scratch(void **ptr)
+{
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess)
+            return err;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return hipSuccess;
+}
 
 int sample_splits(int R, int V)
 {
