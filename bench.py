@@ -110,11 +110,13 @@ def make_layer(torch, dg, shape, l: int, dev, layout: str = "tiled", keep_master
     """Layer l of a workload as the benchmark runs it: fp32 master weights
     drawn on the device (seeded), packed there by dgw4_quantize_rtn, the
     tiled copies made by dgw4_pack_tiled (a load-time conversion, outside
-    every timed region), activations and routing from the host generators.
+    every timed region), activations from the host generator, and the
+    routing from the seeded router logits through the library's router
+    (dgw4_router) on the device.
     ``gu``/``dn`` are the packs in ``layout``, ``gu_other``/``dn_other`` the
     other layout's. keep_masters also returns the fp32 masters (on the
     device), for auditing a layer against the oracle."""
-    from synth import activations, expert_weights_device, routing
+    from synth import activations, expert_weights_device, router_logits
     gw, dw = expert_weights_device(shape, l, dev)
     gu_c = (*dg.quantize_rtn(gw, shape.g_gu), shape.g_gu)
     dn_c = (*dg.quantize_rtn(dw, shape.g_dn), shape.g_dn)
@@ -123,14 +125,15 @@ def make_layer(torch, dg, shape, l: int, dev, layout: str = "tiled", keep_master
     gu_t, dn_t = dg.pack_tiled(gu_c), dg.pack_tiled(dn_c)
     tiled = layout == "tiled"
     x = activations(shape, l)
-    ids, w = routing(shape, l)
+    logits = router_logits(shape, l)
+    ids_d, w_d = dg.router(torch.from_numpy(logits).to(dev), shape.topk)
+    ids = ids_d.cpu().numpy()
     populated = int(np.unique(ids).size)
     return dict(
         gu=gu_t if tiled else gu_c, dn=dn_t if tiled else dn_c,
         gu_other=gu_c if tiled else gu_t, dn_other=dn_c if tiled else dn_t,
-        x=torch.from_numpy(x).to(dev), ids=torch.from_numpy(ids).to(dev),
-        w=torch.from_numpy(w).to(dev), bytes=layer_bytes(shape, populated),
-        populated=populated, masters=masters, x_host=x, ids_host=ids, w_host=w)
+        x=torch.from_numpy(x).to(dev), ids=ids_d, w=w_d, bytes=layer_bytes(shape, populated),
+        populated=populated, masters=masters, x_host=x, logits_host=logits)
 
 
 def graph_replay(torch, dg, step, L, R, out, last, ws, dev) -> dict:
@@ -310,7 +313,7 @@ def cpu_baseline(shape, runs: int = 3):
     use. The rate is scaled to the whole layer (the oracle's work is linear
     in the tokens): layer bytes / (sample seconds x T / sample tokens)."""
     import oracle
-    from synth import activations, expert_weights, routing
+    from synth import activations, expert_weights, router_logits
     t0 = time.time()
     gw, dw = expert_weights(shape, 0)
     gu = (*oracle.quantize_rtn(gw, shape.g_gu), shape.g_gu)
@@ -318,7 +321,8 @@ def cpu_baseline(shape, runs: int = 3):
     dn = (*oracle.quantize_rtn(dw, shape.g_dn), shape.g_dn)
     del dw
     x = activations(shape, 0)
-    ids, w = routing(shape, 0)
+    ids, w = oracle.router(router_logits(shape, 0), shape.topk)
+    w = w.astype(np.float32)
     toks = np.arange(CPU_SAMPLE_TOKENS, dtype=np.int32)
     populated = int(np.unique(ids).size)
     nbytes = layer_bytes(shape, populated)["layer"]

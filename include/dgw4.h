@@ -156,6 +156,28 @@ DGW4_API int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int blo
                int32_t *tile_expert, int32_t *num_padded, void *stream);
 
 /*
+ * dgw4_router — each token's experts and weights from its router logits
+ * ([blog] "Quantisation alone leaves a sparse execution problem": a router
+ * scores the experts per token; the token picks 8 of 128 and the chosen
+ * experts' outputs are weighted). The pages give no formula; the reading:
+ *   ids[t, k]  = the k-th largest of logits[t, :], largest first, equal
+ *                logits ordered by the lower expert id (the topk most
+ *                probable experts, since a softmax is monotone; the choice
+ *                compares the fp32 logits and is exact);
+ *   w[t, k]    = exp(l_k - l_0) / sum_j exp(l_j - l_0) over the chosen
+ *                logits, fp32 (the chosen softmax probabilities
+ *                renormalised to one), the sum taken in k order.
+ * ids and w are the topk_ids / topk_w inputs of dgw4_moe_forward.
+ *   logits  device fp32 [T, E], finite, 4-byte aligned
+ *   ids     device int32 [T, topk] (output); w device fp32 [T, topk] (output)
+ *   T >= 0, 1 <= E <= 1024, 1 <= topk <= min(E, 64)
+ * Returns DGW4_ERR_INVALID_ARG otherwise (or for null/misaligned pointers
+ * with T > 0); T == 0 is a no-op. Enqueued on `stream`, no host sync.
+ */
+DGW4_API int dgw4_router(const float *logits, int T, int E, int topk, int32_t *ids, float *w,
+                         void *stream);
+
+/*
  * dgw4_moe_forward — one routed-expert layer with W4A16 experts.
  * ([kcard] "Grouped MoE": fused_moe_w4_v2(hidden, experts, topk_ids,
  *  topk_weights) with packed gu_q/gu_s/gu_z and dn_q/dn_s/dn_z, one launch for
@@ -223,6 +245,21 @@ DGW4_API int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids,
                                     const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
                                     void *workspace, size_t *ws_bytes, uint16_t *out,
                                     void *stream, void *const *events, int n_events);
+
+/*
+ * dgw4_moe_forward_routed — dgw4_moe_forward from router logits: the router
+ * (dgw4_router) writes each token's ids and weights into the workspace, then
+ * the layer runs on them, all on `stream`. router_logits: device fp32
+ * [T, E], finite, 4-byte aligned; topk <= 64. Other arguments, checks,
+ * workspace (the same size as dgw4_moe_forward's) and results as for
+ * dgw4_moe_forward with the router's ids and weights.
+ */
+DGW4_API int dgw4_moe_forward_routed(const uint16_t *x, const float *router_logits, int T,
+                                     int topk, int E, int d, int m, const uint8_t *gu_q,
+                                     const uint16_t *gu_s, const uint16_t *gu_z, int gu_g,
+                                     const uint8_t *dn_q, const uint16_t *dn_s,
+                                     const uint16_t *dn_z, int dn_g, void *workspace,
+                                     size_t *ws_bytes, uint16_t *out, void *stream);
 
 /*
  * dgw4_moe_experts — the expert stages of dgw4_moe_forward alone (alignment,

@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     quantize_rtn,
     dequant,
     align,
+    router,
     w4a16_linear,
     moe_forward,
     gelu_tanh,

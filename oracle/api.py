@@ -50,6 +50,8 @@ def load():
         lib.orc_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                         P, P, P, I, P, P, P, I, P, I, P, P]
         lib.orc_philox4x32_10.argtypes = [P, P, P]
+        lib.orc_router.restype = I
+        lib.orc_router.argtypes = [P, I, I, I, P, P]
         lib.orc_set_threads.restype = I
         lib.orc_set_threads.argtypes = [I]
         lib.orc_gumbel_uniform.restype = ctypes.c_float
@@ -146,6 +148,18 @@ def align(ids, E: int, block_m: int) -> dict:
         raise ValueError("orc_align: invalid arguments")
     return dict(counts=counts, offsets=offsets, sorted_ids=sorted_ids,
                 tile_expert=tile_expert, num_padded=num_padded)
+
+
+def router(logits, topk: int):
+    """fp32 logits [T, E] -> (ids int32 [T, topk], weights fp64 [T, topk])."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, topk), np.int32)
+    w = np.empty((T, topk), np.float64)
+    rc = load().orc_router(_p(lg), T, E, topk, _p(ids), _p(w))
+    if rc != 0:
+        raise ValueError("orc_router: invalid arguments")
+    return ids, w
 
 
 def gelu_tanh(v: float) -> float:

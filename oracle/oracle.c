@@ -289,6 +289,58 @@ int orc_align(const int32_t *ids, int T, int topk, int E, int bm,
     return 0;
 }
 
+/* --------------------------------------------------------------- router ---- */
+
+/*
+ * Router ([blog] "Quantisation alone leaves a sparse execution problem": a
+ * router scores the experts per token, the token picks 8 of 128 and their
+ * outputs are weighted). The pages give no formula; the reading used:
+ *
+ *   the scores are logits l[t, 0..E-1];
+ *   the token's experts are its topk largest logits, largest first, equal
+ *   logits ordered by the lower expert id (a softmax is monotone, so these
+ *   are the topk most probable experts: the choice compares the fp32 inputs
+ *   and needs no arithmetic at all);
+ *   the weights are the chosen experts' softmax probabilities renormalised
+ *   to sum to one, which is the softmax over the chosen logits alone:
+ *   w[t, k] = exp(l_k - l_0) / sum_j exp(l_j - l_0), l_0 the largest, in fp64.
+ *
+ * logits fp32 [T, E] (finite); ids int32 [T, topk]; w fp64 [T, topk].
+ * Returns 0, or -1 on invalid arguments.
+ */
+int orc_router(const float *logits, int T, int E, int topk, int32_t *ids, double *w)
+{
+    if (T < 0 || E <= 0 || topk <= 0 || topk > E)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < T; ++t) {
+        const float *l = logits + t * (long)E;
+        unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+        if (!taken) {
+            bad = 1;
+            continue;
+        }
+        int32_t *it = ids + t * (long)topk;
+        for (int k = 0; k < topk; ++k) {
+            int best = -1;
+            for (int e = 0; e < E; ++e)        /* ascending e: ties keep the lower id */
+                if (!taken[e] && (best < 0 || l[e] > l[best]))
+                    best = e;
+            taken[best] = 1;
+            it[k] = best;
+        }
+        free(taken);
+        const double l0 = (double)l[it[0]];
+        double den = 0.0;
+        for (int k = 0; k < topk; ++k)
+            den += exp((double)l[it[k]] - l0);
+        for (int k = 0; k < topk; ++k)
+            w[t * (long)topk + k] = exp((double)l[it[k]] - l0) / den;
+    }
+    return bad ? -1 : 0;
+}
+
 /* ----------------------------------------------------------- activation ---- */
 
 /* GELU, tanh form: 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))). The pages

@@ -12,7 +12,7 @@ from .inputs import (  # noqa: F401
     expert_weights,
     expert_weights_device,
     activations,
-    routing,
+    router_logits,
     zipf_prior,
     linear_inputs,
     sampler_logits,

@@ -9,12 +9,8 @@ section names). Values:
 * expert weights  ~ N(0, 0.02) in fp32, layout [E, N, K] (K = contraction);
 * activations     ~ N(0, 1) rounded once to fp16 (numpy's IEEE RN cast);
 * router logits   ~ N(0, 1) in fp32 (plus ln p_rank for the Zipf-skewed
-  workload), softmax, top-k by descending probability with ties to the lower
-  expert id, renormalised so each token's k weights sum to one.
-
-The router is input generation: the layer receives ``topk_ids`` and
-``topk_weights`` as inputs (the kernel card's grouped-MoE call takes them as
-arguments).
+  workload). The routing itself (top-k and weights) is a step of the method:
+  the oracle's router and the library's router compute it from these logits.
 """
 from __future__ import annotations
 
@@ -127,25 +123,15 @@ def zipf_prior(E: int, s: float, seed: int) -> np.ndarray:
     return lnp
 
 
-def routing(shape: LayerShape, layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
-    """topk_ids int32 [T, topk] and topk_weights fp32 [T, topk]; column order is
-    descending router probability."""
+def router_logits(shape: LayerShape, layer: int = 0) -> np.ndarray:
+    """Router logits fp32 [T, E]: N(0, 1), plus ln p_rank(e) for the
+    Zipf-skewed workload."""
     rng = np.random.default_rng(seed_for(shape.index, layer, STREAM_ROUTER))
     logits = rng.standard_normal((shape.T, shape.E), dtype=np.float32)
     if shape.zipf is not None:
         logits += zipf_prior(shape.E, shape.zipf,
                              seed_for(shape.index, layer, STREAM_PERM))[None, :]
-    mx = logits.max(axis=1, keepdims=True)
-    ex = np.exp(logits - mx, dtype=np.float32)
-    p = ex / ex.sum(axis=1, keepdims=True, dtype=np.float32)
-    order = np.argsort(-p, axis=1, kind="stable")        # ties -> lower expert id
-    ids = np.ascontiguousarray(order[:, : shape.topk]).astype(np.int32)
-    pk = np.take_along_axis(p, ids, axis=1).astype(np.float32)
-    tot = np.zeros((shape.T, 1), dtype=np.float32)
-    for k in range(shape.topk):                            # sum in k order
-        tot[:, 0] += pk[:, k]
-    w = (pk / tot).astype(np.float32)
-    return ids, np.ascontiguousarray(w)
+    return logits
 
 
 def linear_inputs(seed: int, T: int, K: int, N: int, std: float = 0.02,

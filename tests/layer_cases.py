@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import w4a16_grouped_moe_amd as dg
-from synth import CONFIGS, LayerShape, activations, expert_weights, routing
+from synth import CONFIGS, LayerShape, activations, expert_weights, router_logits
 
 # The layer's tolerance: max |gpu - ref| <= 1e-2 * max |ref| (fp32 accumulation,
 # fp16 intermediate and output against the fp64 oracle).
@@ -47,6 +47,13 @@ def _to_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
+def route(shape: LayerShape, layer: int = 0):
+    """The layer's routing inputs: the oracle's router on the seeded logits
+    (ids int32, weights rounded once to fp32)."""
+    ids, w = oracle.router(router_logits(shape, layer), shape.topk)
+    return ids, w.astype(np.float32)
+
+
 def pack_both(wf: np.ndarray, g: int):
     """Quantise fp32 [E, N, K] on the host (oracle) and on the device; assert
     the two are bit-identical; return (host pack, device pack)."""
@@ -73,7 +80,7 @@ def build(shape: LayerShape, layer: int = 0, ids=None, w=None, weights=None) -> 
     del dw
     x = activations(shape, layer)
     if ids is None:
-        ids, w = routing(shape, layer)
+        ids, w = route(shape, layer)
     return Layer(shape, x, ids, w, gu_h, dn_h, gu_d, dn_d,
                  _to_dev(x), _to_dev(ids.astype(np.int32)), _to_dev(w.astype(np.float32)))
 

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import w4a16_grouped_moe_amd as dg
-from synth import CONFIGS, routing
+from synth import CONFIGS
 from tests import layer_cases as lc
 
 pytestmark = pytest.mark.gpu
@@ -83,7 +83,7 @@ def test_align_random(bm):
 def test_align_workloads(name):
     shp = CONFIGS[name]
     lc.log(f"[align] workload {name}")
-    ids, _ = routing(shp)
+    ids, _ = lc.route(shp)
     _align_case(ids, shp.E, 32)
 
 

@@ -53,6 +53,11 @@ def test_stack_layer_audit(layer):
     out = torch.empty((sh.T, sh.d), dtype=torch.float16, device=dev)
     dg.moe_forward(ly["x"], ly["ids"], ly["w"], ly["gu"], ly["dn"], workspace=ws, out=out)
     torch.cuda.synchronize()
-    ref = oracle.moe_forward(ly["x_host"], ly["ids_host"], ly["w_host"], host["gate_up"],
+    # the oracle routes the same logits itself; the device router's choice
+    # (which the forward above used) must be the same bit for bit
+    ids, w = oracle.router(ly["logits_host"], sh.topk)
+    assert np.array_equal(ly["ids"].cpu().numpy(), ids), "router ids differ"
+    assert np.allclose(ly["w"].cpu().numpy(), w, rtol=2e-6, atol=0), "router weights differ"
+    ref = oracle.moe_forward(ly["x_host"], ids, w.astype(np.float32), host["gate_up"],
                              host["down"], sh.E)
     lc.assert_close(out.cpu().numpy(), ref, f"stack layer {layer} (tiled, all 256 tokens)")

@@ -7,11 +7,13 @@ from .binding import (  # noqa: F401
     BLOCK_M,
     Dgw4Error,
     align,
+    router,
     align_capacity,
     hbm_read_probe,
     header_functions,
     lib,
     moe_forward,
+    moe_forward_routed,
     pack_tiled,
     WEIGHTS_TILED,
     quantize_rtn,

@@ -70,6 +70,11 @@ def lib():
                                        P, ctypes.POINTER(S), P]
         L.dgw4_sample.restype = I
         L.dgw4_sample.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P, ctypes.POINTER(S), P]
+        L.dgw4_moe_forward_routed.restype = I
+        L.dgw4_moe_forward_routed.argtypes = [P, P, I, I, I, I, I, P, P, P, I, P, P, P, I,
+                                              P, ctypes.POINTER(S), P, P]
+        L.dgw4_router.restype = I
+        L.dgw4_router.argtypes = [P, I, I, I, P, P, P]
         L.dgw4_sample_noalloc.restype = I
         L.dgw4_sample_noalloc.argtypes = [P, I, I, ctypes.c_uint64, P, P, P, P]
         L.dgw4_pack_tiled.restype = I
@@ -226,7 +231,7 @@ def sample_noalloc(logits: torch.Tensor, seed: int = 0, out=None):
                torch.empty(R, dtype=torch.int32, device=dev),
                torch.empty(R, dtype=torch.int32, device=dev))
     h, smp, am = out
-    ptrs = [_dev(t, n, d).__int__() if t is not None else None
+    ptrs = [_dev(t, n, d) if t is not None else None
             for t, n, d in ((h, "entropy", (torch.float32,)), (smp, "sample", (torch.int32,)),
                             (am, "argmax", (torch.int32,)))]
     _check("dgw4_sample_noalloc", lib().dgw4_sample_noalloc(
@@ -243,6 +248,25 @@ def gumbel_argmax_sample(logits: torch.Tensor, seed: int):
     """(Gumbel-max sample, argmax) of each row, one pass."""
     _, smp, am = sample(logits, seed, entropy=False, draw=True)
     return smp, am
+
+
+def router(logits: torch.Tensor, topk: int, ids: torch.Tensor | None = None,
+           w: torch.Tensor | None = None):
+    """Router logits fp32 [T, E] (device) -> (topk_ids int32 [T, topk],
+    topk_w fp32 [T, topk]) as dgw4_router defines them."""
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    pl = _dev(logits, "logits", (torch.float32,))
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    if ids.shape != (T, topk) or w.shape != (T, topk):
+        raise ValueError("ids / w must be [T, topk]")
+    _check("dgw4_router", lib().dgw4_router(pl, T, E, topk, _dev(ids, "ids", (torch.int32,)),
+                                            _dev(w, "w", (torch.float32,)), _stream(logits)))
+    return ids, w
 
 
 def align_capacity(T: int, topk: int, E: int, block_m: int) -> int:
@@ -375,3 +399,35 @@ def moe_experts(x: torch.Tensor, topk_ids: torch.Tensor, gu: tuple, dn: tuple,
     _check("dgw4_moe_experts", lib().dgw4_moe_experts(
         ptrs[0], ptrs[1], T, topk, E, d, m, ptrs[2], ptrs[3], ptrs[4], gg,
         ptrs[5], ptrs[6], ptrs[7], dg, pws, ctypes.byref(n), _stream(x)))
+
+
+def moe_forward_routed(x: torch.Tensor, router_logits: torch.Tensor, topk: int, gu: tuple,
+                       dn: tuple, workspace: torch.Tensor | None = None,
+                       out: torch.Tensor | None = None) -> torch.Tensor:
+    """One routed-expert layer from router logits fp32 [T, E]: the router
+    (dgw4_router), then the layer, in one C-ABI call (dgw4_moe_forward_routed)."""
+    gq, gs, gz, gg = gu
+    dq, ds, dz, dg = dn
+    T, d = x.shape
+    E = gq.shape[0]
+    m = dq.shape[2] * 2
+    if router_logits.shape != (T, E):
+        raise ValueError("router_logits must be [T, E]")
+    if gq.shape != (E, 2 * m, d // 2) or dq.shape != (E, d, m // 2):
+        raise ValueError("packed shapes do not match x")
+    ptrs = [_dev(x, "x", _F16), _dev(router_logits, "router_logits", (torch.float32,)),
+            _dev(gq, "gu_q", (torch.uint8,)), _dev(gs, "gu_s", _F16), _dev(gz, "gu_z", _F16),
+            _dev(dq, "dn_q", (torch.uint8,)), _dev(ds, "dn_s", _F16), _dev(dz, "dn_z", _F16)]
+    need = workspace_bytes(T, topk, E, d, m, gg, dg)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    pws = _dev(workspace, "workspace", (torch.uint8,))
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.float16, device=x.device)
+    pout = _dev(out, "out", _F16)
+    n = ctypes.c_size_t(workspace.numel())
+    _check("dgw4_moe_forward_routed", lib().dgw4_moe_forward_routed(
+        ptrs[0], ptrs[1], T, topk, E, d, m, ptrs[2], ptrs[3], ptrs[4], gg, ptrs[5], ptrs[6],
+        ptrs[7], dg, pws, ctypes.byref(n), pout, _stream(x)))
+    return out
+

@@ -54,7 +54,7 @@ int from_hip(hipError_t e)
 // kernel aligns inside its workgroups and keeps H in LDS, so at the layer's
 // shape only Y is used.
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, rids, rw, total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap)
@@ -74,6 +74,8 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take(2 * sizeof(uint16_t) * (size_t)A * (size_t)d);
+    L.rids = take(sizeof(int32_t) * (size_t)A);       // the router's output (routed forward)
+    L.rw = take(sizeof(float) * (size_t)A);
     L.total = off;
     return L;
 }
@@ -153,7 +155,7 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
                      const uint16_t *gu_z, int gu_garg, const uint8_t *dn_q, const uint16_t *dn_s,
                      const uint16_t *dn_z, int dn_garg, void *workspace, size_t *ws_bytes,
                      uint16_t *out, void *stream, void *const *events, int n_events,
-                     bool with_combine)
+                     bool with_combine, const float *router_logits = nullptr)
 {
     int gu_g = 0, dn_g = 0, gu_tiled = 0, dn_tiled = 0;
     if (!split_group(gu_garg, gu_g, gu_tiled) || !split_group(dn_garg, dn_g, dn_tiled))
@@ -193,7 +195,12 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     }
     if (!gu_q || !gu_s || !gu_z || !dn_q || !dn_s || !dn_z)
         return DGW4_ERR_INVALID_ARG;
-    if (T > 0 && (!x || !topk_ids || (with_combine && (!topk_w || !out))))
+    if (router_logits && topk > 64)
+        return DGW4_ERR_INVALID_ARG;
+    if (T > 0 && (!x || (!topk_ids && !router_logits) ||
+                  (with_combine && !router_logits && !topk_w) || (with_combine && !out)))
+        return DGW4_ERR_INVALID_ARG;
+    if (router_logits && !aligned(router_logits, 4))
         return DGW4_ERR_INVALID_ARG;
     if (!aligned(workspace, kAlign) || !aligned(x, 16) || !aligned(gu_q, 16) ||
         !aligned(dn_q, 16) || !aligned(gu_s, 16) || !aligned(gu_z, 16) || !aligned(dn_s, 16) ||
@@ -251,6 +258,15 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     hipError_t err = mark(0);
     if (err != hipSuccess)
         return from_hip(err);
+    if (router_logits) {
+        // the router's ids and weights into the workspace, then the layer on them
+        int32_t *rids = reinterpret_cast<int32_t *>(ws + L.rids);
+        float *rw = reinterpret_cast<float *>(ws + L.rw);
+        if ((err = dgw4::launch_router(router_logits, T, E, topk, rids, rw, st)) != hipSuccess)
+            return from_hip(err);
+        topk_ids = rids;
+        topk_w = rw;
+    }
     const bool fused = dgw4::layer_fused(gu, gu_g, dn, dn_g, E);
     if (fused) {
         // alignment, gate_up and down in one launch: marks 1, 2 and 3 all follow it
@@ -302,6 +318,19 @@ int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *to
                             dn_s, dn_z, dn_g, workspace, ws_bytes, out, stream, nullptr, 0, true);
 }
 
+int dgw4_moe_forward_routed(const uint16_t *x, const float *router_logits, int T, int topk,
+                            int E, int d, int m, const uint8_t *gu_q, const uint16_t *gu_s,
+                            const uint16_t *gu_z, int gu_g, const uint8_t *dn_q,
+                            const uint16_t *dn_s, const uint16_t *dn_z, int dn_g,
+                            void *workspace, size_t *ws_bytes, uint16_t *out, void *stream)
+{
+    if (workspace && T > 0 && !router_logits)
+        return DGW4_ERR_INVALID_ARG;
+    return moe_forward_impl(x, nullptr, nullptr, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g, dn_q,
+                            dn_s, dn_z, dn_g, workspace, ws_bytes, out, stream, nullptr, 0, true,
+                            router_logits);
+}
+
 int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T, int topk, int E, int d,
                      int m, const uint8_t *gu_q, const uint16_t *gu_s, const uint16_t *gu_z,
                      int gu_g, const uint8_t *dn_q, const uint16_t *dn_s, const uint16_t *dn_z,
@@ -310,6 +339,17 @@ int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T, int topk
     return moe_forward_impl(x, topk_ids, nullptr, T, topk, E, d, m, gu_q, gu_s, gu_z, gu_g, dn_q,
                             dn_s, dn_z, dn_g, workspace, ws_bytes, nullptr, stream, nullptr, 0,
                             false);
+}
+
+int dgw4_router(const float *logits, int T, int E, int topk, int32_t *ids, float *w, void *stream)
+{
+    if (T < 0 || E < 1 || E > dgw4::kMaxExperts || topk < 1 || topk > E || topk > 64)
+        return DGW4_ERR_INVALID_ARG;
+    if (T == 0)
+        return DGW4_OK;
+    if (!logits || !ids || !w || !aligned(logits, 4) || !aligned(ids, 4) || !aligned(w, 4))
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_router(logits, T, E, topk, ids, w, (hipStream_t)stream));
 }
 
 int dgw4_sample_noalloc(const float *logits, int R, int V, uint64_t seed, float *entropy,

@@ -39,6 +39,12 @@ hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long
                         int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
                         hipStream_t stream);
 
+// Router: ids int32 [T, topk] (the topk largest logits, largest first, ties
+// to the lower id) and w fp32 [T, topk] (softmax over the chosen logits) from
+// logits fp32 [T, E]; 1 <= topk <= min(E, 64), E <= kMaxExperts.
+hipError_t launch_router(const float *logits, int T, int E, int topk, int32_t *ids, float *w,
+                         hipStream_t stream);
+
 // LDS one GEMM workgroup needs for contraction width K and group size g.
 size_t gemm_lds_bytes(bool gated, int K, int g);
 
