@@ -507,6 +507,34 @@ def main() -> int:
     kern_bytes = sum(layers[i % L]["bytes"]["gate_up"] + layers[i % L]["bytes"]["down"]
                      for i in range(S)) / S
 
+    # The layer from router logits (dgw4_moe_forward_routed: the router
+    # kernel, then the layer) over the same steps, and the router alone.
+    logits_d = [torch.from_numpy(layers[i]["logits_host"]).to(dev) for i in range(L)]
+    rids = torch.empty((shape.T, shape.topk), dtype=torch.int32, device=dev)
+    rw = torch.empty((shape.T, shape.topk), dtype=torch.float32, device=dev)
+
+    def routed(i):
+        ly = layers[i % L]
+        dg.moe_forward_routed(ly["x"], logits_d[i % L], shape.topk, ly["gu"], ly["dn"],
+                              workspace=ws, out=out)
+
+    def router_only(i):
+        dg.router(logits_d[i % L], shape.topk, rids, rw)
+
+    routed_us = {}
+    for name, fn, n in (("routed_forward", routed, K), ("router_alone", router_only, S)):
+        for i in range(L):
+            fn(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        routed_us[name] = round(e0.elapsed_time(e1) * 1e3 / n, 2)
+    log(f"[bench] from router logits: {routed_us['routed_forward']} us per layer; "
+        f"router alone {routed_us['router_alone']} us back to back")
+
     moved = sum(layers[i % L]["bytes"]["layer"] for i in range(K))
     ms_per_step = total_ms / K
     gbps = moved / (total_ms * 1e-3) / 1e9
@@ -558,6 +586,12 @@ def main() -> int:
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_layer": layers[0]["bytes"]["layer"],
         "stage_us": stage_us,
+        "from_router_logits": {
+            "us_per_layer": routed_us["routed_forward"],
+            "router_alone_us": routed_us["router_alone"],
+            "note": ("dgw4_moe_forward_routed over the same steps: the router kernel "
+                     "(top-8 of fp32 logits [T, E] and weights) before the layer"),
+        },
         "eager_sweeps": spread,
         "graph_replay": graph,
         "hbm_probe": probe,

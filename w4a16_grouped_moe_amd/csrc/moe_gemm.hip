@@ -1480,29 +1480,33 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
     }
 }
 
-// ---- down alone (gate_up at another group size): workgroup = (tile, 1408
-// output columns = 88 row tiles); wave w streams row tiles w, w + 11, ...,
-// w + 77, P tiles ahead, each tile's output stored when done; H from the
-// gate_up launch, the tile's rows from the alignment kernel.
+// ---- down alone (gate_up at another group size, or down's own group size
+// 128 at K = 768): workgroup = (tile, 1408 output columns = 88 row tiles);
+// wave w streams row tiles w, w + 11, ..., w + 77, P tiles ahead, each
+// tile's output stored when done; H from the gate_up launch, the tile's rows
+// from the alignment kernel. Instantiated for (g, K/g) = (64, 11) and
+// (128, 6): the same body for both group sizes.
 constexpr int kDn4Tiles = 8;                     // row tiles per wave
 constexpr int kDn4Rows = kL4Waves * kDn4Tiles * 16;   // 1408 weight rows per workgroup
 constexpr int kDn4Ahead = 2;
-constexpr int kDn4ALoads = 4;                    // 32 rows x 88 segments over 704 threads
 
+// activation segments per thread: 32 rows x K/8 segments over 704 threads
+constexpr int down4_a_loads(int K) { return (kBlockM * (K / 8) + kL4Threads - 1) / kL4Threads; }
+
+template <int G, int NG>
 constexpr size_t down4_lds_bytes()
 {
-    return sizeof(uint4) * kBlockM * (kDnGroups * 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * kDnGroups;
+    return sizeof(uint4) * kBlockM * (NG * G / 8 + 1) + 2 * sizeof(uint16_t) * kDn4Rows * NG;
 }
 
-template <int NMS, bool TL, bool NT>
+template <int G, int NG, int NMS, bool TL, bool NT>
 __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, int cb,
-                                           const uint4 (&av)[kDn4ALoads], int fid)
+                                           const uint4 (&av)[down4_a_loads(NG * G)], int fid)
 {
-    constexpr int G = 64;
     constexpr int P = kDn4Ahead;
-    constexpr int NG = kDnGroups;
-    constexpr int K = NG * G;                      // 704
-    constexpr int kWords = 2;
+    constexpr int K = NG * G;                      // 704 or 768
+    constexpr int kALoads = down4_a_loads(K);
+    constexpr int kWords = G / 32;
     constexpr int a_pitch = K / 8 + 1;
     constexpr int seg_row = K / 8;
     const int tid = threadIdx.x;
@@ -1523,8 +1527,8 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     // ---- 1. scale/zero of the block's rows, then the first weight tiles
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, (uint32_t)p.n_w * (uint32_t)NG * 2u);
-    constexpr int kSzSeg = kDn4Rows * NG * 2 / 16;                  // 1936
-    constexpr int kSzLoads = (kSzSeg + kL4Threads - 1) / kL4Threads;   // 3
+    constexpr int kSzSeg = kDn4Rows * NG * 2 / 16;                  // 1936 or 1056
+    constexpr int kSzLoads = (kSzSeg + kL4Threads - 1) / kL4Threads;   // 3 or 2
     const uint32_t sz_base = (uint32_t)(rt0 * 16 * NG) * 2u;
     uint4 sv[kSzLoads], zv[kSzLoads];
 #pragma unroll
@@ -1570,7 +1574,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
         }
     }
 #pragma unroll
-    for (int i = 0; i < kDn4ALoads; ++i) {
+    for (int i = 0; i < kALoads; ++i) {
         const int x = i * kL4Threads + tid;
         const int r = x / seg_row, sg = x - r * seg_row;
         if (r < 16 * NMS)
@@ -1588,7 +1592,7 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     uint16_t *Y = static_cast<uint16_t *>(p.out);
 
     // ---- 3. stream the wave's 8 row tiles, P ahead; each tile's 16 x 32
-    // outputs are stored as soon as its 11 groups are done
+    // outputs are stored as soon as its NG groups are done
 #pragma unroll
     for (int j = 0; j < kDn4Tiles; ++j) {
         const int st = j % P;
@@ -1639,9 +1643,10 @@ __device__ __forceinline__ void down4_body(const GemmArgs &p, int e, int row0, i
     }
 }
 
-template <bool TL>
+template <int G, int NG, bool TL>
 __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
 {
+    constexpr int kALoads = down4_a_loads(NG * G);
     // workgroup -> (column half, tile), both halves of a tile on one XCD; the
     // tile's activation rows and assignment ids are requested before its
     // descriptor is known
@@ -1652,9 +1657,9 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
         return;
     const int tid = threadIdx.x;
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)p.K * 2u);
-    uint4 av[kDn4ALoads];
+    uint4 av[kALoads];
 #pragma unroll
-    for (int i = 0; i < kDn4ALoads; ++i)
+    for (int i = 0; i < kALoads; ++i)
         av[i] = load16(ra, down_a_off(p, tile * kBlockM, i * kL4Threads + tid), 0);
     int fid = p.A;
     if (tid < kBlockM)
@@ -1665,14 +1670,14 @@ __global__ void __launch_bounds__(kL4Threads) down4_kernel(GemmArgs p)
     const bool more = tile_valid(info.y) > 16;
     if (TL && tile_count(info.y) == 1) {
         if (more)
-            down4_body<2, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
+            down4_body<G, NG, 2, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
         else
-            down4_body<1, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
+            down4_body<G, NG, 1, TL, TL>(p, info.x, tile * kBlockM, cb, av, fid);
     } else {
         if (more)
-            down4_body<2, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
+            down4_body<G, NG, 2, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
         else
-            down4_body<1, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
+            down4_body<G, NG, 1, TL, false>(p, info.x, tile * kBlockM, cb, av, fid);
     }
 }
 
@@ -1694,20 +1699,22 @@ bool layer_shape_gate_up(const GemmArgs &a, int g)
     return g == 128 && a.K == kGuSteps * 256 && a.n_out == 2 * kGu4Cols && a.n_w == 2 * a.n_out;
 }
 
+// the wide-block down body: d = 2816 outputs at (g, K) = (64, 704) or (128, 768)
 bool layer_shape_down(const GemmArgs &a, int g)
 {
-    return g == 64 && a.K == kDnGroups * 64 && a.n_out == 2 * kDn4Rows && a.n_w == a.n_out;
+    return ((g == 64 && a.K == kDnGroups * 64) || (g == 128 && a.K == 6 * 128)) &&
+           a.n_out == 2 * kDn4Rows && a.n_w == a.n_out;
 }
 
-template <bool TL>
+template <int G, int NG, bool TL>
 hipError_t launch_down4(const GemmArgs &a, hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;             // one per instantiation
-    hipError_t err = allow_lds(down4_kernel<TL>, down4_lds_bytes(), allowed);
+    hipError_t err = allow_lds(down4_kernel<G, NG, TL>, down4_lds_bytes<G, NG>(), allowed);
     if (err != hipSuccess)
         return err;
     const int tiles = (a.max_tiles + kXcds - 1) / kXcds * kXcds;
-    down4_kernel<TL><<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes(), stream>>>(a);
+    down4_kernel<G, NG, TL><<<dim3(tiles * 2), dim3(kL4Threads), down4_lds_bytes<G, NG>(), stream>>>(a);
     return hipGetLastError();
 }
 
@@ -1803,8 +1810,12 @@ hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
 {
     if (a.max_tiles == 0)
         return hipSuccess;
-    if (layer_shape_down(a, g))
-        return a.tiled ? launch_down4<true>(a, stream) : launch_down4<false>(a, stream);
+    if (layer_shape_down(a, g)) {
+        if (g == 64)
+            return a.tiled ? launch_down4<64, kDnGroups, true>(a, stream)
+                           : launch_down4<64, kDnGroups, false>(a, stream);
+        return a.tiled ? launch_down4<128, 6, true>(a, stream) : launch_down4<128, 6, false>(a, stream);
+    }
     if (a.tiled)
         return g == 128 ? launch_down_g<128, true>(a, stream) : launch_down_g<64, true>(a, stream);
     return g == 128 ? launch_down_g<128, false>(a, stream) : launch_down_g<64, false>(a, stream);
@@ -1819,8 +1830,8 @@ hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
 
 bool layer_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g, int E)
 {
-    return layer_shape_gate_up(gu, gu_g) && layer_shape_down(dn, dn_g) && gu.tiled == dn.tiled &&
-           E <= kMaxExperts;
+    return layer_shape_gate_up(gu, gu_g) && dn_g == 64 && layer_shape_down(dn, dn_g) &&
+           gu.tiled == dn.tiled && E <= kMaxExperts;
 }
 
 hipError_t launch_layer(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,

@@ -12,10 +12,11 @@
 // logits: w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), fp32, summed in k
 // order.
 //
-// One wave per token: lane i holds logits i, i + 64, ...; each of the topk
-// rounds takes the wave's largest untaken logit (ties to the lower id) with
-// a butterfly of (value, id) pairs, so every lane ends with the same ordered
-// list; lane k writes id k and weight k.
+// One wave per token, no sequential rounds: the token's logits go to a slot
+// of LDS, every lane ranks the logits it holds against all of them (rank =
+// how many logits are larger, or equal at a lower id), and the logit of rank
+// k < topk is choice k. The weights' exp terms are laid out in choice order
+// and summed in that order by every lane.
 #include "dgw4_internal.hpp"
 
 #include <cmath>
@@ -24,10 +25,10 @@ namespace dgw4 {
 namespace {
 
 constexpr int kRouterWaves = 4;                  // tokens per workgroup
-constexpr int kRouterPer = kMaxExperts / 64;     // logits per lane, at most
 
-// (v, e) beats (v2, e2): the larger value, or the same value at a smaller id
-__device__ inline bool beats(float v, int e, float v2, int e2)
+// (v, e) ranks before (v2, e2): the larger value, or the same value at a
+// smaller id
+__device__ inline bool before(float v, int e, float v2, int e2)
 {
     return v > v2 || (v == v2 && e < e2);
 }
@@ -38,65 +39,57 @@ __global__ void __launch_bounds__(kRouterWaves * 64) router_kernel(const float *
                                                                   int32_t *__restrict__ ids,
                                                                   float *__restrict__ w)
 {
+    __shared__ float s_l[kRouterWaves][PER * 64];    // the token's logits
+    __shared__ float s_x[kRouterWaves][64];          // exp terms in choice order
+    __shared__ float s_v[kRouterWaves][64];          // chosen logits in choice order
     const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * kRouterWaves + (threadIdx.x >> 6);
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * kRouterWaves + wv;
     if (t >= T)
-        return;
+        return;                                      // whole waves: no barrier below
     const float *l = logits + (size_t)t * E;
     float v[PER];
-    bool live[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = lane + 64 * j;
-        live[j] = e < E;
-        v[j] = live[j] ? l[e] : 0.0f;
+        v[j] = e < E ? l[e] : 0.0f;
+        if (e < E)
+            s_l[wv][e] = v[j];
     }
-    float my_v = 0.0f;                               // lane k keeps choice k
-    int my_e = 0;
-    float top = 0.0f;
-    for (int k = 0; k < topk; ++k) {
-        // this lane's best untaken logit (ascending id: ties keep the lower)
-        float bv = 0.0f;
-        int be = -1;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    int rank[PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int e = lane + 64 * j;
-            if (live[j] && (be < 0 || beats(v[j], e, bv, be))) {
-                bv = v[j];
-                be = e;
-            }
-        }
-        // the wave's best: a butterfly over (value, id); lanes without an
-        // untaken logit carry id -1 and lose to any other
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, 64);
-            const int oe = __shfl_xor(be, off, 64);
-            if (oe >= 0 && (be < 0 || beats(ov, oe, bv, be))) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if (k == 0)
-            top = bv;
-        if (lane == k) {
-            my_v = bv;
-            my_e = be;
-        }
-        // the owner lane marks it taken
+    for (int j = 0; j < PER; ++j)
+        rank[j] = 0;
+    for (int e2 = 0; e2 < E; ++e2) {                 // the same address for all lanes: a broadcast
+        const float v2 = s_l[wv][e2];
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            if (be == lane + 64 * j)
-                live[j] = false;
+            rank[j] += before(v2, e2, v[j], lane + 64 * j);
     }
-    // weights: exp(l_k - l_0) / sum_j exp(l_j - l_0), the sum in k order
+    // choice k: its id, its logit; the largest logit is choice 0
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int e = lane + 64 * j;
+        if (e < E && rank[j] < topk) {
+            ids[(size_t)t * topk + rank[j]] = e;
+            s_v[wv][rank[j]] = v[j];
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    const float top = s_v[wv][0];
+    if (lane < topk)
+        s_x[wv][lane] = expf(s_v[wv][lane] - top);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), the sum in choice order
     float den = 0.0f;
     for (int k = 0; k < topk; ++k)
-        den = __fadd_rn(den, expf(__shfl(my_v, k, 64) - top));
-    if (lane < topk) {
-        ids[(size_t)t * topk + lane] = my_e;
-        w[(size_t)t * topk + lane] = __fdiv_rn(expf(my_v - top), den);
-    }
+        den = __fadd_rn(den, s_x[wv][k]);
+    if (lane < topk)
+        w[(size_t)t * topk + lane] = __fdiv_rn(s_x[wv][lane], den);
 }
 
 }  // namespace
@@ -111,7 +104,7 @@ hipError_t launch_router(const float *logits, int T, int E, int topk, int32_t *i
     if (E <= 128)
         router_kernel<2><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, w);
     else
-        router_kernel<kRouterPer><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, w);
+        router_kernel<kMaxExperts / 64><<<grid, block, 0, stream>>>(logits, T, E, topk, ids, w);
     return hipGetLastError();
 }
 
