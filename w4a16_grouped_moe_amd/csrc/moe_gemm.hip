@@ -1050,27 +1050,31 @@ __device__ void layer_tile_rows(const int32_t *__restrict__ ids, int A, int e, c
 }
 
 // ---- 2. gate_up: workgroup = (tile, 352 output columns); wave w owns pairs
-// 2w and 2w + 1 (columns col0 + 32 w .. + 32) and computes them one after the
-// other: pass 0 walks all of K for pair 2w, pass 1 for pair 2w + 1. The 22
-// line steps run as straight-line code with the loads P steps ahead across
-// the pass boundary; each pass restages the same activation slices.
-// H = gelu_tanh(gate) * up goes to the LDS frame (see kHPitch). rows fills
-// the flat ids of the activation rows once the first weight loads are out;
-// after_k runs once the last step's weights are consumed, before the last
-// epilogue: the down phase issues its first loads there.
+// 2w and 2w + 1 (columns col0 + 32 w .. + 32: 16 gate columns and the
+// matching 16 up columns each, four weight row tiles) and computes both in
+// one pass over K, one group of 128 per step: 22 steps, straight-line, each
+// loading 16 bytes per lane of each of the four tiles (4 KB per wave), the
+// weights P steps and the activations P - 1 steps ahead. Each step's
+// activation slice (the tile's rows, 256 bytes each) is staged in LDS once
+// for the 11 waves, so every activation byte is read once per workgroup.
+// H = gelu_tanh(gate) * up goes to the LDS frame (see kHPitch). rows() ranks
+// the tile's rows into s_rows once the first weight loads are out; after_k
+// runs once the last step's weights are consumed, before the epilogue: the
+// down phase issues its first loads there.
+constexpr int kGu4Seg = 16;                      // 16-byte activation segments per row and step
+constexpr int kGu4Pitch = kGu4Seg + 1;           // +16 B per row against bank conflicts
+
 template <int NMS, bool TL, bool NT, class Rows, class AfterK>
 __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, Rows &&rows,
-                                              AfterK &&after_k)
+                                              const int *s_rows, AfterK &&after_k)
 {
     constexpr int G = 128;
-    constexpr int P = kGu4Ahead;
+    constexpr int P = 3;                           // weight steps in flight
     constexpr int PX = 2;                          // activation stages, issued P - 1 steps ahead
-    constexpr int SG = 2;                          // groups per line step
     constexpr int kWords = 4;
-    constexpr int NG = kGu4Groups;
+    constexpr int NG = kGu4Groups;                 // 22 steps, one group each
     constexpr int K = kGuSteps * 256;
-    constexpr int NQ = 2 * kGuSteps;               // line steps of both passes
-    constexpr int XLD = 2;                         // 32 rows x 32 segments over 704 threads
+    constexpr int NT4 = 4;                         // weight row tiles per wave: gate 0, up 0, gate 1, up 1
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1081,14 +1085,14 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, 
     const int col0 = cb * kGu4Cols;
 
     extern __shared__ uint4 lds[];
-    uint4 *lds_x = lds;                                             // [2][33][kStepPitch]
+    uint4 *lds_x = lds;                                             // [2][33][kGu4Pitch]
     uint16_t *lds_s = reinterpret_cast<uint16_t *>(lds + 2 * kGu4XRows * kStepPitch);   // [704 rows][NG]
     uint16_t *lds_z = lds_s + kGu4SzSeg * 8;
     uint16_t *lds_h = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(lds) + layer_gate_up_lds_bytes());
+    static_assert(kGu4Pitch <= kStepPitch, "activation stage fits its area");
 
-    // ---- 1. scale/zero of the 352 gate and 352 up rows, then per step the
-    // activations and the weights (in issue order: scale/zero, then step by
-    // step)
+    // ---- 1. scale/zero of the 352 gate and 352 up rows, the weights of the
+    // first steps, then (once the rows are known) the activations
     const uint32_t sz_bytes = (uint32_t)p.n_w * (uint32_t)NG * 2u;
     const rsrc_t rs = make_rsrc(p.s + wexp * (size_t)NG, sz_bytes);
     const rsrc_t rz = make_rsrc(p.z + wexp * (size_t)NG, sz_bytes);
@@ -1109,51 +1113,44 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, 
     }
 
     const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
-    // pass c: gate rows col0 + 32 wave + 16 c + lrow, then the matching up rows
+    // tile u: pair c = u / 2 (columns col0 + 32 wave + 16 c ..), gate (u even) or up
     auto in_range = [&](int c) { return wave * 32 + c * 16 + lrow; };
-    auto wvoff = [&](int c, int u) { return wq_lane_off<G, TL>((u ? n_out : 0) + col0 + in_range(c), lane, K); };
-    Frag<G> bq[P][2][SG];
-    auto issue_w = [&](int st, int q) {            // global step q = 11 pass + step
-        const int c = q / kGuSteps, s = q % kGuSteps;
+    auto sz_row = [&](int u) { return (u & 1) * kGu4Cols + in_range(u >> 1); };   // row in lds_s/lds_z
+    uint32_t wvoff[NT4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const uint32_t voff = wvoff(c, u);
+    for (int u = 0; u < NT4; ++u)
+        wvoff[u] = wq_lane_off<G, TL>(((u & 1) ? n_out : 0) + col0 + in_range(u >> 1), lane, K);
+    Frag<G> bq[P][NT4];
+    auto issue_w = [&](int st, int s) {
 #pragma unroll
-            for (int h = 0; h < SG; ++h)
-                bq[st][u][h] = load_frag<G, NT>(rq, voff, wq_group_off<G, TL>(s * SG + h));
-        }
+        for (int u = 0; u < NT4; ++u)
+            bq[st][u] = load_frag<G, NT>(rq, wvoff[u], wq_group_off<G, TL>(s));
     };
-    // the weights of the first steps go out before the tile's rows are known
-    issue_w(0, 0);
 #pragma unroll
-    for (int q = 1; q < P; ++q)
-        issue_w(q, q);
+    for (int s = 0; s < P; ++s)
+        issue_w(s, s);
     __builtin_amdgcn_sched_barrier(0);
-    int fidr[2];
-    rows(fidr);
+    rows();
+    // activation slices: thread -> (row tid / 16, 16-byte segment tid % 16)
+    // of a step; rows past 16 NMS, pad rows and threads past row 32 read
+    // nothing
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
-    const int xseg = tid % kStepSeg;
-    uint32_t xoff[XLD];
-#pragma unroll
-    for (int i = 0; i < XLD; ++i) {
-        const int r = (i * kL4Threads + tid) / kStepSeg;
-        xoff[i] = r < NMS * 16 && fidr[i] < p.A
-                      ? (uint32_t)(fidr[i] / p.topk) * (uint32_t)K * 2u + (uint32_t)xseg * 16u
-                      : kOutOfRange;
-    }
-    uint4 xr[PX][XLD];
-    auto issue_x = [&](int st, int q) {
-        const int s = q % kGuSteps;
-#pragma unroll
-        for (int i = 0; i < XLD; ++i)
-            xr[st][i] = load16(ra, xoff[i] != kOutOfRange ? xoff[i] + (uint32_t)s * 512u : kOutOfRange, 0);
+    const int xseg = tid % kGu4Seg;
+    const int xrow = tid / kGu4Seg;
+    const int xfid = s_rows[min(xrow, kBlockM - 1)];
+    const uint32_t xoff = xrow < NMS * 16 && xfid < p.A
+                              ? (uint32_t)(xfid / p.topk) * (uint32_t)K * 2u + (uint32_t)xseg * 16u
+                              : kOutOfRange;
+    uint4 xr[PX];
+    auto issue_x = [&](int st, int s) {
+        xr[st] = load16(ra, xoff != kOutOfRange ? xoff + (uint32_t)s * 256u : kOutOfRange, 0);
     };
-    // prologue: w(0) w(1) w(2) (above), x(0) x(1); in step q: x(q + PX) then
-    // w(q + P), so waiting for a step's activations never waits for later
+    // prologue: w(0) w(1) w(2) (above), x(0) x(1); in step s: x(s + PX) then
+    // w(s + P), so waiting for a step's activations never waits for later
     // weights
 #pragma unroll
-    for (int q = 0; q < PX; ++q)
-        issue_x(q, q);
+    for (int s = 0; s < PX; ++s)
+        issue_x(s, s);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. scale/zero into LDS (made visible by the first step's barrier;
@@ -1169,100 +1166,100 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, 
         }
     }
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NT4][NMS];
+#pragma unroll
+    for (int u = 0; u < NT4; ++u)
+#pragma unroll
+        for (int ms = 0; ms < NMS; ++ms)
+            acc[u][ms] = zero4;
 
-    // ---- 3. two passes of 11 line steps, straight-line
+    // ---- 3. 22 steps of one group, straight-line
+#pragma unroll
+    for (int s = 0; s < NG; ++s) {
+        const int st = s % P;
+        uint4 *xb = lds_x + (s & 1) * kGu4XRows * kStepPitch;
+        if (xrow <= kBlockM)                        // row 32 takes the rows past the tile
+            xb[xrow * kGu4Pitch + xseg] = permute8(xr[s % PX]);
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        // an opaque LDS offset per step keeps the compiler from hoisting
+        // later steps' scale/zero and activation reads into registers
+        int loff = 0;
+        asm volatile("" : "+v"(loff));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {              // pair c: its gate and up tiles
+            float scale[2];
+            f16x2 c1024[2], c64[2];
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+                const int row = sz_row(2 * c + v);
+                zero_point_consts(lds_z[loff + row * NG + s], c1024[v], c64[v]);
+                scale[v] = (float)__builtin_bit_cast(_Float16, lds_s[loff + row * NG + s]);
+            }
+            f32x4 part[2][NMS];
+#pragma unroll
+            for (int t = 0; t < kWords; ++t) {
+                f16x8 bop[2];
+#pragma unroll
+                for (int v = 0; v < 2; ++v)
+                    bop[v] = dequant8(frag_word<G>(bq[st][2 * c + v], t), c1024[v], c64[v]);
+                const int seg = quarter * (G / 32) + t;
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+                    const f16x8 aop = __builtin_bit_cast(f16x8, xb[loff + (ms * 16 + lrow) * kGu4Pitch + seg]);
+#pragma unroll
+                    for (int v = 0; v < 2; ++v)
+                        part[v][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            aop, bop[v], t == 0 ? zero4 : part[v][ms], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+                for (int ms = 0; ms < NMS; ++ms) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[2 * c + v][ms][i] += scale[v] * part[v][ms][i];
+                    // pin the accumulation here: otherwise the compiler
+                    // sinks it to the epilogue and keeps every partial live
+                    asm volatile("" : "+v"(acc[2 * c + v][ms]));
+                }
+        }
+        if (s + PX < NG)
+            issue_x(s % PX, s + PX);
+        if (s + P < NG)
+            issue_w(st, s + P);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    after_k();
+    __builtin_amdgcn_sched_barrier(0);
+    // epilogue: H = gelu_tanh(gate) * up in fp16, permuted per 8, into the
+    // LDS frame at column 32 cb + local column (each wave owns its columns);
+    // rows past the tile's valid rows hold gelu(0) * 0 = 0. The lane's
+    // indices are recomputed from an opaque copy of the thread id (kept
+    // across the loop they would be spilled, and their reload would wait for
+    // every load in flight).
+    int etid = threadIdx.x;
+    asm volatile("" : "+v"(etid));
+    const int equarter = (etid & 63) >> 4;
+    const int elrow = etid & 15;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-        const int lds_row0 = in_range(c);                 // gate row in lds_s/lds_z
-        const int lds_row1 = kGu4Cols + in_range(c);      // up row
-        f32x4 acc[2][NMS];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-            for (int ms = 0; ms < NMS; ++ms)
-                acc[u][ms] = zero4;
-#pragma unroll
-        for (int s = 0; s < kGuSteps; ++s) {
-            const int q = c * kGuSteps + s;
-            const int st = q % P;
-            uint4 *xb = lds_x + (q & 1) * kGu4XRows * kStepPitch;
-#pragma unroll
-            for (int i = 0; i < XLD; ++i) {
-                const int r = min((i * kL4Threads + tid) / kStepSeg, kBlockM);
-                xb[r * kStepPitch + xseg] = permute8(xr[q % PX][i]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            __syncthreads();
-            // an opaque LDS offset per step keeps the compiler from hoisting
-            // later steps' scale/zero and activation reads into registers
-            int loff = 0;
-            asm volatile("" : "+v"(loff));
-#pragma unroll
-            for (int h = 0; h < SG; ++h) {
-                const int gi = s * SG + h;
-                float scale[2];
-                f16x2 c1024[2], c64[2];
-                zero_point_consts(lds_z[loff + lds_row0 * NG + gi], c1024[0], c64[0]);
-                zero_point_consts(lds_z[loff + lds_row1 * NG + gi], c1024[1], c64[1]);
-                scale[0] = (float)__builtin_bit_cast(_Float16, lds_s[loff + lds_row0 * NG + gi]);
-                scale[1] = (float)__builtin_bit_cast(_Float16, lds_s[loff + lds_row1 * NG + gi]);
-                f32x4 part[2][NMS];
-#pragma unroll
-                for (int t = 0; t < kWords; ++t) {
-                    f16x8 bop[2];
-#pragma unroll
-                    for (int u = 0; u < 2; ++u)
-                        bop[u] = dequant8(frag_word<G>(bq[st][u][h], t), c1024[u], c64[u]);
-                    const int seg = h * (G / 8) + quarter * (G / 32) + t;
-#pragma unroll
-                    for (int ms = 0; ms < NMS; ++ms) {
-                        const f16x8 aop = __builtin_bit_cast(f16x8, xb[loff + (ms * 16 + lrow) * kStepPitch + seg]);
-#pragma unroll
-                        for (int u = 0; u < 2; ++u)
-                            part[u][ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                aop, bop[u], t == 0 ? zero4 : part[u][ms], 0, 0, 0);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u)
-#pragma unroll
-                    for (int ms = 0; ms < NMS; ++ms) {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[u][ms][i] += scale[u] * part[u][ms][i];
-                        // pin the accumulation here: otherwise the compiler
-                        // sinks it to the epilogue and keeps every partial live
-                        asm volatile("" : "+v"(acc[u][ms]));
-                    }
-            }
-            if (q + PX < NQ)
-                issue_x(q % PX, q + PX);
-            if (q + P < NQ)
-                issue_w(st, q + P);
-        }
-        if (c == 1) {
-            __builtin_amdgcn_sched_barrier(0);
-            after_k();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // epilogue of the pass: H = gelu_tanh(gate) * up in fp16, permuted per
-        // 8, into the LDS frame at column 32 cb + local column (each wave owns
-        // its columns); rows past the tile's valid rows hold gelu(0) * 0 = 0
-        const int hcol = kBlockM * cb + permuted_col(in_range(c));   // 32 cb is a multiple of 8
+        const int hcol = kBlockM * cb + permuted_col(wave * 32 + c * 16 + elrow);   // 32 cb: a multiple of 8
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = ms * 16 + quarter * 4 + i;
-                const float h = gelu_tanh(acc[0][ms][i]) * acc[1][ms][i];
-                lds_h[r * kHPitch + hcol] = __builtin_bit_cast(uint16_t, (_Float16)h);
+                const int r = ms * 16 + equarter * 4 + i;
+                const float hv = gelu_tanh(acc[2 * c][ms][i]) * acc[2 * c + 1][ms][i];
+                lds_h[r * kHPitch + hcol] = __builtin_bit_cast(uint16_t, (_Float16)hv);
             }
         }
     }
     // the frame's 32 columns outside this half: zero (rows 16 NMS .. 31 are
     // never read)
-    if (tid < kBlockM * 4) {
-        const int r = tid >> 2, sg = tid & 3;
+    if (etid < kBlockM * 4) {
+        const int r = etid >> 2, sg = etid & 3;
         const int col = (cb == 0 ? kGu4Cols : 0) + sg * 8;
         *reinterpret_cast<uint4 *>(lds_h + r * kHPitch + col) = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -1417,15 +1414,15 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
     }
 }
 
-// Rows: a callable that ranks the tile's rows into s_rows and fills fidr
-// (the activation rows' flat ids for gate_up's staging), run once the first
-// weight loads are out.
+// Rows: a callable that ranks the tile's rows into s_rows, run once the
+// first weight loads are out.
 template <int NMS, bool TL, bool NT, class Rows>
 __device__ __forceinline__ void layer_body(const GemmArgs &gu, const GemmArgs &dn, int e, int h,
                                            Rows &&rows, const int *s_rows, int valid)
 {
     DownKsPrefetch pf;
-    gate_up4_body<NMS, TL, NT>(gu, e, h, rows, [&]() { down_ks_prefetch<TL, NT>(dn, e, h, pf); });
+    gate_up4_body<NMS, TL, NT>(gu, e, h, rows, s_rows,
+                               [&]() { down_ks_prefetch<TL, NT>(dn, e, h, pf); });
     down_ks_body<NMS, TL, NT>(dn, e, h, s_rows, valid, pf);
 }
 
@@ -1449,12 +1446,7 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
     const int e = layer_tile_find(ids, gu.A, E, tile, ts, s_cnt, s_wsum, s_rows, s_info);
     if (e < 0)
         return;
-    auto rows = [&](int (&fidr)[2]) {
-        layer_tile_rows(ids, gu.A, e, ts, s_wsum, s_rows);
-        const int tid = threadIdx.x;
-        fidr[0] = s_rows[tid / kStepSeg];
-        fidr[1] = s_rows[min((kL4Threads + tid) / kStepSeg, kBlockM - 1)];
-    };
+    auto rows = [&]() { layer_tile_rows(ids, gu.A, e, ts, s_wsum, s_rows); };
     const int valid = ts.valid;
     // tiled weights of an expert that no other tile reads stream past the
     // caches; those of an expert with several tiles stay cacheable
