@@ -98,6 +98,13 @@ __device__ inline uint4 load16(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// 8-byte store at voff; dropped past the end of the buffer.
+__device__ inline void store8(rsrc_t r, uint32_t voff, uint2 v)
+{
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, voff, 0, 0);
+}
+
 template <int G>
 struct Frag;                     // one lane's share of one group of one weight row
 template <>
@@ -1266,16 +1273,21 @@ __device__ __forceinline__ void gate_up4_body(const GemmArgs &p, int e, int cb, 
 }
 
 // ---- 3. down, the workgroup's half of the contraction into all outputs.
-// Wave w streams row tiles w, w + 11, ..., w + 165 (16 of the 176 row tiles of
-// d = 2816), P tiles ahead; a tile covers the half's 6 local groups (global
-// groups 5 h .. 5 h + 5). With each tile's weights the wave loads the tile's
-// 16 rows of scales and zero points (352 contiguous bytes each: lanes 0-21
-// and 22-43 take 16 bytes apiece) and lays them out in a slot of LDS of its
-// own, from which its lanes read what they need: no workgroup-wide staging
-// and no barrier. The MFMA takes the weights as its row operand, so a lane
-// ends with four consecutive output columns of one assignment row and
-// stores them (8 bytes of the fp16 partial) as soon as the tile is done.
-constexpr int kKsTiles = 16;                     // row tiles per wave
+// The 176 row tiles of d = 2816 are shared out at run time: wave w starts
+// with tiles w, w + 11 and w + 22, and each time it finishes one it takes the
+// next unclaimed tile from a counter in LDS, so waves that the memory path
+// serves faster do more tiles and all of them stay busy to the end. A tile
+// covers the half's 6 local groups (global groups 5 h .. 5 h + 5). With each
+// tile's weights the wave loads the tile's 16 rows of scales and zero points
+// (352 contiguous bytes each: lanes 0-21 and 22-43 take 16 bytes apiece) and
+// lays them out in a slot of LDS of its own, from which its lanes read what
+// they need: no workgroup-wide staging and no barrier. The MFMA takes the
+// weights as its row operand, so a lane ends with four consecutive output
+// columns of one assignment row and stores them (8 bytes of the fp16
+// partial) as soon as the tile is done.
+constexpr int kKsRowTiles = 176;                 // row tiles of d = 2816
+constexpr int kKsMaxTiles = 20;                  // row tiles one wave may take
+static_assert(kL4Waves * kKsMaxTiles >= kKsRowTiles, "the capped waves still take every tile");
 constexpr int kKsGroups = 6;                     // local groups per half
 constexpr int kKsAhead = 3;                      // row tiles in flight per wave
 constexpr int kKsSzLanes = 16 * kDnGroups * 2 / 16;   // 22 lanes of 16 bytes per array
@@ -1296,41 +1308,71 @@ __device__ inline bool ks_idle(int h, int j, int quarter)
     return h == 0 ? (j == kKsGroups - 1 && quarter >= 2) : (j == 0 && quarter < 2);
 }
 
-// Loads of row tile j (of this wave) into prefetch stage st.
-template <bool TL, bool NT>
-__device__ __forceinline__ void down_ks_issue(const GemmArgs &p, int e, int h, int wave, int lane,
-                                              DownKsPrefetch &pf, int st, int j)
+// A lane's part of the down addresses, the same for every row tile: the
+// tile enters them as rt * (bytes of a row tile).
+struct DownKsLane {
+    uint32_t wq;                                 // weight offset in row tile 0
+    uint32_t wq_split;                           // the same for the split group (out of range if idle)
+    const uint16_t *sz;                          // its 16 bytes of row tile 0's scales or zeros
+};
+
+template <bool TL>
+__device__ __forceinline__ DownKsLane down_ks_lane(const GemmArgs &p, int e, int h, int lane)
 {
     constexpr int K = kDnGroups * 64;
     constexpr int NG = kDnGroups;
-    const size_t wexp = (size_t)e * p.n_w;
-    const rsrc_t rq = make_rsrc(p.q + wexp * (size_t)(K / 2), (uint32_t)p.n_w * (uint32_t)(K / 2));
-    const int quarter = lane >> 4;
-    const int rt = wave + j * kL4Waves;           // row tile
-    const uint32_t voff = j < kKsTiles ? wq_lane_off<64, TL>(rt * 16 + (lane & 15), lane, K) : kOutOfRange;
-#pragma unroll
-    for (int g = 0; g < kKsGroups; ++g)
-        pf.bq[st][g] = load_frag<64, NT>(rq, ks_idle(h, g, quarter) ? kOutOfRange : voff,
-                                         wq_group_off<64, TL>(g + 5 * h));
-    if (j < kKsTiles && lane < 2 * kKsSzLanes) {
-        const uint16_t *src = (lane < kKsSzLanes ? p.s : p.z) + wexp * NG + (size_t)rt * 16 * NG;
-        pf.sz[st] = *reinterpret_cast<const uint4 *>(src + (lane % kKsSzLanes) * 8);
-    }
+    DownKsLane l;
+    l.wq = wq_lane_off<64, TL>(lane & 15, lane, K);
+    l.wq_split = ks_idle(h, h == 0 ? kKsGroups - 1 : 0, lane >> 4) ? kOutOfRange : l.wq;
+    const int sl = lane < 2 * kKsSzLanes ? lane : 0;   // lanes past 43 repeat lane 0's load
+    l.sz = (sl < kKsSzLanes ? p.s : p.z) + (size_t)e * p.n_w * NG + (sl % kKsSzLanes) * 8;
+    return l;
 }
+
+// Loads of row tile rt into prefetch stage st; past the last tile the weight
+// loads read nothing and the scale/zero load repeats the last tile's (it is
+// issued on every path, so the loads in flight are the same on all of them).
+template <bool TL, bool NT>
+__device__ __forceinline__ void down_ks_issue(const GemmArgs &p, int e, int h, const DownKsLane &l,
+                                              DownKsPrefetch &pf, int st, int rt)
+{
+    constexpr int K = kDnGroups * 64;
+    constexpr int NG = kDnGroups;
+    constexpr uint32_t kTileBytes = 16 * K / 2;    // one row tile of the weights
+    const rsrc_t rq = make_rsrc(p.q + (size_t)e * p.n_w * (size_t)(K / 2),
+                                (uint32_t)p.n_w * (uint32_t)(K / 2));
+    const bool live = rt < kKsRowTiles;
+    const uint32_t tile_off = (uint32_t)rt * kTileBytes;
+    const uint32_t v = live ? l.wq + tile_off : kOutOfRange;
+    const uint32_t vs = live && l.wq_split != kOutOfRange ? l.wq_split + tile_off : kOutOfRange;
+#pragma unroll
+    for (int g = 0; g < kKsGroups; ++g) {
+        const bool split = g == (h == 0 ? kKsGroups - 1 : 0);
+        pf.bq[st][g] = load_frag<64, NT>(rq, split ? vs : v, wq_group_off<64, TL>(g + 5 * h));
+    }
+    const int srt = live ? rt : kKsRowTiles - 1;
+    pf.sz[st] = *reinterpret_cast<const uint4 *>(l.sz + (size_t)srt * 16 * NG);
+}
+
+// The first row tile of prefetch stage j of wave w (the rest are claimed).
+__device__ __forceinline__ int ks_first_tile(int wave, int j) { return wave + j * kL4Waves; }
 
 template <bool TL, bool NT>
 __device__ __forceinline__ void down_ks_prefetch(const GemmArgs &p, int e, int h, DownKsPrefetch &pf)
 {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const DownKsLane l = down_ks_lane<TL>(p, e, h, tid & 63);
 #pragma unroll
     for (int j = 0; j < kKsAhead; ++j)
-        down_ks_issue<TL, NT>(p, e, h, wave, tid & 63, pf, j, j);
+        down_ks_issue<TL, NT>(p, e, h, l, pf, j, ks_first_tile(wave, j));
 }
 
+// s_next: the LDS counter of claimed row tiles, set by this function before
+// its first barrier.
 template <int NMS, bool TL, bool NT>
 __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, const int *s_rows,
-                                             int valid, DownKsPrefetch &pf)
+                                             int valid, DownKsPrefetch &pf, int *s_next)
 {
     constexpr int G = 64;
     constexpr int P = kKsAhead;
@@ -1348,6 +1390,8 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
     char *slots = reinterpret_cast<char *>(lds) + wave * P * kKsSlot;   // this wave's, over gate_up's staging
     const uint16_t *lds_h = reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(lds) +
                                                                layer_gate_up_lds_bytes());
+    if (tid == 0)
+        *s_next = kL4Waves * P;                    // the first P tiles of every wave are fixed
     // H complete; every wave is done with gate_up's staging
     __syncthreads();
     int dst[NMS];                                  // output rows (flat ids) of this lane's MFMA rows
@@ -1356,28 +1400,49 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
         dst[ms] = ms * 16 + lrow < valid ? s_rows[ms * 16 + lrow] : -1;
 
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    uint16_t *Y = static_cast<uint16_t *>(p.out) + (size_t)h * (size_t)p.A * (size_t)n_out;
+    const DownKsLane l = down_ks_lane<TL>(p, e, h, lane);
+    // the partial's rows: lane offsets in bytes, out of range (store dropped)
+    // for rows past the tile; a row tile adds 32 bytes per tile index
+    const rsrc_t ry = make_rsrc(static_cast<uint16_t *>(p.out) + (size_t)h * (size_t)p.A * (size_t)n_out,
+                                (uint32_t)p.A * (uint32_t)n_out * 2u);
+    uint32_t yoff[NMS];
 #pragma unroll
-    for (int j = 0; j < kKsTiles; ++j) {
+    for (int ms = 0; ms < NMS; ++ms)
+        yoff[ms] = dst[ms] >= 0 ? ((uint32_t)dst[ms] * (uint32_t)n_out + (uint32_t)quarter * 4u) * 2u
+                                : 0x80000000u;
+    int rt[P];                                     // row tile in each prefetch stage (uniform)
+#pragma unroll
+    for (int st = 0; st < P; ++st)
+        rt[st] = ks_first_tile(wave, st);
+    // Tile j of the wave comes from stage j % P. Claims only grow and the
+    // stages are used in the order they were filled, so the first empty
+    // stage ends the wave's work. Straight-line code with forward exits
+    // only: the loads in flight are known at every point, so each wait
+    // covers just the stage it needs.
+#pragma unroll
+    for (int j = 0; j < kKsMaxTiles; ++j) {
         const int st = j % P;
-        // the tile's scales [16][11] then zero points [16][11] into the slot;
-        // the same wave reads them back (its LDS operations run in order)
+        const int cur = rt[st];
+        if (cur >= kKsRowTiles)
+            break;
+        // the tile's scales [16][11] then zero points [16][11] into the
+        // slot; the same wave reads them back (its LDS operations run in
+        // order)
         char *slot = slots + st * kKsSlot;
         if (lane < 2 * kKsSzLanes)
             *reinterpret_cast<uint4 *>(slot + lane * 16) = pf.sz[st];
         const uint16_t *ls = reinterpret_cast<const uint16_t *>(slot);
         const uint16_t *lz = ls + 16 * NG;
-        int aoff = 0;                              // keeps the H reads per tile (see gate_up)
+        int aoff = 0;                          // keeps the H reads per tile (see gate_up)
         asm volatile("" : "+v"(aoff));
-        const int srow = (wave + j * kL4Waves) * 16;   // first weight row (output column)
         f32x4 out[NMS];
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms)
             out[ms] = zero4;
 #pragma unroll
         for (int g = 0; g < kKsGroups; ++g) {
-            asm volatile("" : "+v"(aoff));         // and per group: no hoisting of later groups' reads
-            const int gg = g + 5 * h;              // global group
+            asm volatile("" : "+v"(aoff));     // and per group: no hoisting of later groups' reads
+            const int gg = g + 5 * h;          // global group
             f16x2 c1024, c64;
             zero_point_consts(lz[lrow * NG + gg], c1024, c64);
             float sc[4];
@@ -1393,7 +1458,8 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
                 for (int ms = 0; ms < NMS; ++ms) {
                     const f16x8 aop = *reinterpret_cast<const f16x8 *>(
                         lds_h + aoff + (ms * 16 + lrow) * kHPitch + col);
-                    prt[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop, aop, t == 0 ? zero4 : prt[ms], 0, 0, 0);
+                    prt[ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop, aop, t == 0 ? zero4 : prt[ms],
+                                                                     0, 0, 0);
                 }
             }
 #pragma unroll
@@ -1404,12 +1470,20 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
                 asm volatile("" : "+v"(out[ms]));   // pin the accumulation (see gate_up)
             }
         }
-        down_ks_issue<TL, NT>(p, e, h, wave, lane, pf, st, j + P);
-        const int col = srow + quarter * 4;
+        // claim the wave's next row tile and start its loads in this stage
+        // (a wave that has reached its cap claims no more)
+        if (j + P < kKsMaxTiles) {
+            int next = 0;
+            if (lane == 0)
+                next = atomicAdd(s_next, 1);
+            next = __builtin_amdgcn_readfirstlane(next);
+            rt[st] = next;
+            down_ks_issue<TL, NT>(p, e, h, l, pf, st, next);
+        }
+        // output columns cur * 16 + 4 quarter .. + 3 of the lane's rows
 #pragma unroll
         for (int ms = 0; ms < NMS; ++ms)
-            if (dst[ms] >= 0)
-                *reinterpret_cast<uint2 *>(Y + (size_t)dst[ms] * n_out + col) = pack_f16x4(out[ms]);
+            store8(ry, yoff[ms] + (uint32_t)cur * 32u, pack_f16x4(out[ms]));
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -1418,12 +1492,12 @@ __device__ __forceinline__ void down_ks_body(const GemmArgs &p, int e, int h, co
 // first weight loads are out.
 template <int NMS, bool TL, bool NT, class Rows>
 __device__ __forceinline__ void layer_body(const GemmArgs &gu, const GemmArgs &dn, int e, int h,
-                                           Rows &&rows, const int *s_rows, int valid)
+                                           Rows &&rows, const int *s_rows, int valid, int *s_next)
 {
     DownKsPrefetch pf;
     gate_up4_body<NMS, TL, NT>(gu, e, h, rows, s_rows,
                                [&]() { down_ks_prefetch<TL, NT>(dn, e, h, pf); });
-    down_ks_body<NMS, TL, NT>(dn, e, h, s_rows, valid, pf);
+    down_ks_body<NMS, TL, NT>(dn, e, h, s_rows, valid, pf, s_next);
 }
 
 // Workgroup -> (half, tile), both halves of a tile on one XCD (consecutive
@@ -1437,6 +1511,7 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
     __shared__ int s_wsum[kL4Waves];
     __shared__ int s_rows[kBlockM];
     __shared__ int s_info[4];
+    __shared__ int s_next;
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
     const int h = slot % 2;
     const int tile = slot / 2 * kXcds + xcd;
@@ -1456,18 +1531,18 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
     if (valid > 16) {
         if (nt) {
             asm volatile("; streaming weights");
-            layer_body<2, TL, TL>(gu, dn, e, h, rows, s_rows, valid);
+            layer_body<2, TL, TL>(gu, dn, e, h, rows, s_rows, valid, &s_next);
         } else {
             asm volatile("; cached weights");
-            layer_body<2, TL, false>(gu, dn, e, h, rows, s_rows, valid);
+            layer_body<2, TL, false>(gu, dn, e, h, rows, s_rows, valid, &s_next);
         }
     } else {
         if (nt) {
             asm volatile("; streaming weights");
-            layer_body<1, TL, TL>(gu, dn, e, h, rows, s_rows, valid);
+            layer_body<1, TL, TL>(gu, dn, e, h, rows, s_rows, valid, &s_next);
         } else {
             asm volatile("; cached weights");
-            layer_body<1, TL, false>(gu, dn, e, h, rows, s_rows, valid);
+            layer_body<1, TL, false>(gu, dn, e, h, rows, s_rows, valid, &s_next);
         }
     }
 }
@@ -1481,6 +1556,7 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
 constexpr int kDn4Tiles = 8;                     // row tiles per wave
 constexpr int kDn4Rows = kL4Waves * kDn4Tiles * 16;   // 1408 weight rows per workgroup
 constexpr int kDn4Ahead = 2;
+static_assert(kKsRowTiles * 16 == 2 * kDn4Rows, "the layer kernel's down covers all d outputs");
 
 // activation segments per thread: 32 rows x K/8 segments over 704 threads
 constexpr int down4_a_loads(int K) { return (kBlockM * (K / 8) + kL4Threads - 1) / kL4Threads; }
@@ -1822,8 +1898,10 @@ hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
 
 bool layer_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g, int E)
 {
+    // (the layer kernel stores each Y partial through 32-bit byte offsets
+    // below 2^31)
     return layer_shape_gate_up(gu, gu_g) && dn_g == 64 && layer_shape_down(dn, dn_g) &&
-           gu.tiled == dn.tiled && E <= kMaxExperts;
+           gu.tiled == dn.tiled && E <= kMaxExperts && (long long)dn.A * dn.n_out * 2 < (1LL << 31);
 }
 
 hipError_t launch_layer(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,
