@@ -244,7 +244,9 @@ def bench_linear(torch, dg, dev, args) -> int:
         "bytes_per_call": nbytes,
         # 2 T K N FLOP over 392 MB of weights is 4 T = 1024 FLOP per byte,
         # far past the fp16 ridge (2.5 PFLOP/s over 8 TB/s = 312): MFMA-bound
-        "roofline": {"kernel": f"linear_kernel<128, {str(args.weight_layout == 'tiled').lower()}>",
+        "roofline": {"kernel": (f"linear_wide_kernel<128, 22, {str(args.weight_layout == 'tiled').lower()}, "
+                                f"{str(args.weight_layout == 'tiled').lower()}> (256-row blocks, each "
+                                f"weight formed once per block)"),
                      "bound": "mfma", "achieved": round(tflops, 1),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),

@@ -6,7 +6,9 @@ zero) equals F.linear(x, dequant(W)). Checked here: the device packing
 against the oracle's bit for bit, the output element by element within
 max|err| <= 1e-2 * max|ref| on shapes with ragged row tiles, idle column
 tiles and both group sizes, and exactly on one-hot rows, where each output is
-one dequantised weight rounded once to fp16.
+one dequantised weight rounded once to fp16. From 128 rows on the library
+takes its many-row kernel (fp16 weights (q - z) * s formed in registers,
+accumulated in fp32), covered by the same checks.
 """
 import numpy as np
 import pytest
@@ -40,6 +42,14 @@ def _pack(w: np.ndarray, g: int):
     dict(T=1, K=2816, N=704, g=128),      # one row
     dict(T=70, K=512, N=48, g=128),       # last column block with idle waves
     dict(T=40, K=1536, N=96, g=64),       # 24 groups of 64 per row
+    # from 128 rows on, the many-row kernel (256-row blocks, 128 columns per
+    # workgroup): several row blocks with a ragged last one and a ragged last
+    # column block, an idle second row half, the generic K loop at both
+    # group sizes
+    dict(T=513, K=2816, N=2112, g=128),
+    dict(T=128, K=1024, N=256, g=128),
+    dict(T=200, K=2816, N=384, g=64),
+    dict(T=300, K=768, N=144, g=128),
 ])
 def test_linear_matches_oracle(case):
     T, K, N, g = case["T"], case["K"], case["N"], case["g"]
@@ -52,14 +62,16 @@ def test_linear_matches_oracle(case):
     lc.assert_close(y.cpu().numpy(), ref, f"linear T={T} K={K} N={N} g={g}")
 
 
-@pytest.mark.parametrize("g", [64, 128])
-def test_linear_one_hot_rows_are_exact(g):
+@pytest.mark.parametrize("g,rows", [(64, 10), (128, 10), (64, 160), (128, 160)])
+def test_linear_one_hot_rows_are_exact(g, rows):
     # row r of x is the unit vector e_{c_r}: y[r, n] = deq(W)[n, c_r], a small
-    # integer times an fp16 scale (exact in fp32), rounded once to fp16
+    # integer times an fp16 scale (exact in fp32), rounded once to fp16; 160
+    # rows take the many-row kernel
     K, N = 1024, 160
     _, w = linear_inputs(7, 1, K, N)
     host, dev = _pack(w, g)
-    cols = np.array([0, 1, 7, 8, 63, 64, 127, 128, 500, 1023], dtype=np.int64)
+    base = np.array([0, 1, 7, 8, 63, 64, 127, 128, 500, 1023], dtype=np.int64)
+    cols = np.resize(base, rows) if rows > base.size else base[:rows]
     x = np.zeros((cols.size, K), np.float16)
     x[np.arange(cols.size), cols] = 1.0
     y = dg.w4a16_linear(torch.from_numpy(x).cuda(), dev)
@@ -80,3 +92,28 @@ def test_linear_zero_rows():
     assert torch.count_nonzero(y).item() == 0
     empty = dg.w4a16_linear(torch.zeros((0, K), dtype=torch.float16, device="cuda"), dev)
     assert empty.shape == (0, N)
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_linear_many_rows_are_independent_and_deterministic(g):
+    # the many-row kernel (from 128 rows on) stages 256-row activation blocks
+    # shared by all its waves: an output row depends on its own input row
+    # only (changing every other row leaves it bit for bit the same), and a
+    # call repeated gives the same bits
+    T, K, N = 300, 2816, 512
+    x, w = linear_inputs(31 + g, T, K, N)
+    _, dev = _pack(w, g)
+    xd = torch.from_numpy(x).cuda()
+    y1 = dg.w4a16_linear(xd, dev).clone()
+    y2 = dg.w4a16_linear(xd, dev).clone()
+    x2 = xd.clone()
+    x2[100:] = torch.flip(x2[100:], dims=[0])                # rows 100.. permuted
+    x2[:100:3] = 0                                           # and some early rows zeroed
+    y3 = dg.w4a16_linear(x2, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    keep = torch.ones(100, dtype=torch.bool, device="cuda")
+    keep[::3] = False
+    assert torch.equal(y3[:100][keep].view(torch.int16), y1[:100][keep].view(torch.int16))
+    assert torch.equal(y3[100:].view(torch.int16), torch.flip(y1[100:], dims=[0]).view(torch.int16))
+    assert torch.count_nonzero(y3[:100:3]).item() == 0

@@ -127,7 +127,8 @@ def test_forward_tiled_unfused_layer_shape():
     lc.assert_close(_forward_pair(L), lc.oracle_forward(L), "tiled unfused (all 64 tokens)")
 
 
-@pytest.mark.parametrize("g,T,K,N", [(128, 37, 2816, 1408), (64, 70, 704, 2816), (128, 1, 512, 48)])
+@pytest.mark.parametrize("g,T,K,N", [(128, 37, 2816, 1408), (64, 70, 704, 2816), (128, 1, 512, 48),
+                                     (128, 300, 2816, 1408), (64, 256, 1024, 384)])
 def test_linear_tiled_equals_canonical(g, T, K, N):
     x, wf = linear_inputs(11, T, K, N)
     q, s, z = dg.quantize_rtn(torch.from_numpy(wf).cuda(), g)
