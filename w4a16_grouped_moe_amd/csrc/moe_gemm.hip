@@ -618,13 +618,19 @@ size_t linear_wide_lds_bytes(int K)
     return linear_wide_x_bytes<G>() + 2 * sizeof(uint16_t) * (size_t)kLwCols * (size_t)(K / G);
 }
 
-// Physical slot of logical 16-byte segment seg of activation row r: rows
-// that share LDS banks (16 / SEGS of them per 256-byte bank cycle) are
-// XOR-spread over the row's slots.
+// Physical slot of logical 16-byte segment seg of activation row r, an XOR
+// swizzle so that a fragment read (16 rows per quarter-wave, the four
+// quarters at segments 4 apart) spreads over the banks. With 16 slots per
+// row the XOR value is r's low four bits permuted (bit 0 to bit 2): the 16
+// rows of a quarter take 16 distinct slots, and rows of opposite parity take
+// slots of opposite bit 2, so two quarters served together never meet.
 template <int SEGS>
 __device__ __forceinline__ int lw_slot(int r, int seg)
 {
-    return seg ^ ((r / (16 / SEGS)) % SEGS);
+    if constexpr (SEGS == 16)
+        return seg ^ (((r & 1) << 2) | ((r >> 1) & 3) | (r & 8));
+    else
+        return seg ^ ((r / (16 / SEGS)) % SEGS);
 }
 
 // f(S), f(S + 1), ..., f(E - 1) as straight-line code, whatever the body's
@@ -763,9 +769,14 @@ __attribute__((amdgpu_waves_per_eu(2))) linear_wide_kernel(GemmArgs p)
 
     auto step = [&](int s, int st) __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);       // nothing moves between steps
-        const uint4 *xb = lds_x + (s & 1) * kLwRows * SEGS;
         int loff = 0;                                    // opaque per step: no hoisted reads
         asm volatile("" : "+v"(loff));
+        // the slice's buffer as an opaque base, so that the row offsets of the
+        // fragment reads stay immediate (the second buffer starts past what
+        // an LDS instruction's offset field reaches)
+        int xbase = (s & 1) * kLwRows * SEGS;
+        asm volatile("" : "+v"(xbase));
+        const uint4 *xb = lds_x + xbase;
         {
             f16x2 cmix[kLwNs], s2[kLwNs];
 #pragma unroll
@@ -775,46 +786,48 @@ __attribute__((amdgpu_waves_per_eu(2))) linear_wide_kernel(GemmArgs p)
                 cmix[ns] = as_h2(zb | (zb << 16)) + f16x2{(_Float16)1024.0f, (_Float16)64.0f};
                 s2[ns] = as_h2(sb | (sb << 16));
             }
-            // per k-slice t the 16-row blocks, one activation fragment feeding
-            // both tiles' MFMAs; between them the two tiles' fragments of
-            // k-slice t + 1 are formed (vector work beside the matrix work),
-            // and the next block's activation fragment is read while a
-            // block's MFMAs run
+            // the step's (k-slice t, 16-row block) pairs in order, each one
+            // activation fragment feeding both tiles' MFMAs; fragments are
+            // read kAhead pairs before use (LDS latency is several pairs'
+            // MFMA time), and between the MFMAs of k-slice t the two tiles'
+            // weight fragments of t + 1 are formed
+            constexpr int kPairs = kWords * kLwMs;
+            constexpr int kAheadA = 4;
+            auto aread = [&](int i) {
+                const int t = i / kLwMs, r = (i % kLwMs) * 16 + lrow;   // row within the block
+                return __builtin_bit_cast(f16x8, xb[r * SEGS + lw_slot<SEGS>(r, quarter * kWords + t)]);
+            };
             f16x8 bop[kLwNs], bnext[kLwNs];
 #pragma unroll
             for (int ns = 0; ns < kLwNs; ++ns)
                 bop[ns] = dequant8_scaled(frag_word<G>(bq[st][ns], 0), cmix[ns], s2[ns]);
+            f16x8 af[kPairs];
 #pragma unroll
-            for (int t = 0; t < kWords; ++t) {
-                if (t == kWords / 2) {
+            for (int i = 0; i < kAheadA; ++i)
+                af[i] = aread(i);
+#pragma unroll
+            for (int i = 0; i < kPairs; ++i) {
+                const int t = i / kLwMs, ms = i % kLwMs;
+                if (t == kWords / 2 && ms == 0) {
                     // the first half of the next slice is in: stage it, load the second
                     stage_x((s + 1) & 1, 0);
                     issue_x(s + 1, 1);
                 }
-                const int seg = quarter * kWords + t;
-                auto aread = [&](int ms) {
-                    const int r = ms * 16 + lrow;            // row within the block
-                    return __builtin_bit_cast(f16x8, xb[loff + r * SEGS + lw_slot<SEGS>(r, seg)]);
-                };
-                f16x8 anext = aread(0);
+                if (i + kAheadA < kPairs)
+                    af[i + kAheadA] = aread(i + kAheadA);
 #pragma unroll
-                for (int ms = 0; ms < kLwMs; ++ms) {
-                    const f16x8 aop = anext;
-                    if (ms + 1 < kLwMs)
-                        anext = aread(ms + 1);
-#pragma unroll
-                    for (int ns = 0; ns < kLwNs; ++ns)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[ns], aop, acc[ms][ns], 0, 0, 0);
-                    constexpr int kPer = kLwMs / kLwNs;      // blocks per next fragment
-                    if (t + 1 < kWords && ms % kPer == kPer - 1) {
-                        const int ns = ms / kPer;
-                        bnext[ns] = dequant8_scaled(frag_word<G>(bq[st][ns], t + 1), cmix[ns], s2[ns]);
-                    }
+                for (int ns = 0; ns < kLwNs; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bop[ns], af[i], acc[ms][ns], 0, 0, 0);
+                constexpr int kPer = kLwMs / kLwNs;          // blocks per next fragment
+                if (t + 1 < kWords && ms % kPer == kPer - 1) {
+                    const int ns = ms / kPer;
+                    bnext[ns] = dequant8_scaled(frag_word<G>(bq[st][ns], t + 1), cmix[ns], s2[ns]);
                 }
-                if (t + 1 < kWords)
+                if (t + 1 < kWords && ms == kLwMs - 1)
 #pragma unroll
                     for (int ns = 0; ns < kLwNs; ++ns)
                         bop[ns] = bnext[ns];
+                __builtin_amdgcn_sched_barrier(0);   // keep the reads where they are issued
             }
         }
         issue_w(st, s + P);
