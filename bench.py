@@ -194,6 +194,23 @@ def read_probe(torch, dg, dev, gib: int = 2, reps: int = 10) -> dict:
             "gbps": round(gbps, 1)}
 
 
+def mfma_probe(torch, dg, dev, iters: int = 20000, reps: int = 5) -> dict:
+    """On-box dense fp16 MFMA ceiling: the library's whole-chip MFMA probe
+    (register operands, no memory traffic)."""
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    dg.mfma_probe(iters // 10, sink)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    flops = sum(dg.mfma_probe(iters, sink) for _ in range(reps))
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    return {"kind": "whole-chip v_mfma_f32_16x16x32_f16 on register operands (dgw4_mfma_probe)",
+            "tflops": round(tflops, 1)}
+
+
 def bench_linear(torch, dg, dev, args) -> int:
     """The dense W4A16 linear at an LM-head shape: x fp16 [256, 2816] against
     one packed [262144, 2816] matrix (392 MB of nibbles, scales and zeros:
@@ -232,6 +249,9 @@ def bench_linear(torch, dg, dev, args) -> int:
     flops = 2 * T * K * N
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[linear] {steps} calls: {ms * 1e3:.1f} us each, {gbps:.1f} GB/s, {tflops:.1f} TFLOP/s")
+    probe = mfma_probe(torch, dg, dev)
+    probe["pct_of_probe"] = round(100 * tflops / probe["tflops"], 2)
+    log(f"[linear] MFMA probe {probe['tflops']} TFLOP/s; the linear at {probe['pct_of_probe']}% of it")
     print(json.dumps({
         "metric": "us per dense W4A16 linear + achieved HBM GB/s (% of 8 TB/s)",
         "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
@@ -242,6 +262,7 @@ def bench_linear(torch, dg, dev, args) -> int:
                    "weight_layout": args.weight_layout},
         "us_per_call": round(ms * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
+        "mfma_probe": probe,
         # 2 T K N FLOP over 392 MB of weights is 4 T = 1024 FLOP per byte,
         # far past the fp16 ridge (2.5 PFLOP/s over 8 TB/s = 312): MFMA-bound
         "roofline": {"kernel": (f"linear_wide_kernel<128, 22, {str(args.weight_layout == 'tiled').lower()}, "

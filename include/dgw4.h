@@ -359,6 +359,20 @@ DGW4_API int dgw4_sample_noalloc(const float *logits, int R, int V, uint64_t see
  */
 DGW4_API int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
+/*
+ * dgw4_mfma_probe — a measurement aid, not a step of the layer: every wave of
+ * a whole-chip launch (two 512-thread workgroups per compute unit) runs
+ * `iters` rounds of eight independent v_mfma_f32_16x16x32_f16 on operands
+ * held in registers, with no memory traffic, so that the elapsed time on
+ * `stream` gives the dense fp16 matrix rate this device sustains. *flops
+ * (host memory) receives the launch's floating-point operations (2 x 16 x 16
+ * x 32 per MFMA). The sums are folded into one word, stored to sink[0] only
+ * if it equals 0x9E3779B9, which keeps the work from being optimised away.
+ * iters >= 1; sink: device memory of at least 4 bytes. Returns
+ * DGW4_ERR_INVALID_ARG otherwise, DGW4_ERR_HIP if the launch fails.
+ */
+DGW4_API int dgw4_mfma_probe(int iters, uint32_t *sink, double *flops, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -108,6 +108,18 @@ def test_read_probe_rejects():
     assert r(p + 8, 16, p, None) == B.ERR_INVALID_ARG
 
 
+def test_mfma_probe_rejects():
+    # checked on the host before any launch: no iterations, null sink or
+    # FLOP count
+    r = dg.lib().dgw4_mfma_probe
+    p = 1 << 12
+    f = ctypes.c_double(0.0)
+    assert r(0, p, ctypes.byref(f), None) == B.ERR_INVALID_ARG
+    assert r(-5, p, ctypes.byref(f), None) == B.ERR_INVALID_ARG
+    assert r(10, None, ctypes.byref(f), None) == B.ERR_INVALID_ARG
+    assert r(10, p, None, None) == B.ERR_INVALID_ARG
+
+
 def test_linear_rejects():
     # host-side checks before any launch
     f = dg.lib().dgw4_w4a16_linear

@@ -278,6 +278,22 @@ def test_read_probe_runs():
     assert sink.item() == 0 and gbps > 100.0
 
 
+def test_mfma_probe_runs():
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    dg.mfma_probe(200, sink)
+    e0.record()
+    flops = dg.mfma_probe(2000, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert flops == cus * 2 * 8 * 2000 * 8 * 2 * 16 * 16 * 32
+    tflops = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    lc.log(f"[probe] MFMA f16 at {tflops:.0f} TFLOP/s")
+    assert sink.item() == 0 and tflops > 100.0
+
+
 @pytest.mark.parametrize("name", ["down_g64", "down_g128"])
 def test_forward_down_group_variants_every_token(name):
     # the layer's shape with separate gate_up and down launches: down at

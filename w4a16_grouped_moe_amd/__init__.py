@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     router,
     align_capacity,
     hbm_read_probe,
+    mfma_probe,
     header_functions,
     lib,
     moe_forward,

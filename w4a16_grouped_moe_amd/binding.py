@@ -81,6 +81,8 @@ def lib():
         L.dgw4_pack_tiled.argtypes = [P, I, I, I, I, P, P]
         L.dgw4_hbm_read_probe.restype = I
         L.dgw4_hbm_read_probe.argtypes = [P, S, P, P]
+        L.dgw4_mfma_probe.restype = I
+        L.dgw4_mfma_probe.argtypes = [I, P, ctypes.POINTER(ctypes.c_double), P]
         _lib = L
     return _lib
 
@@ -313,6 +315,17 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
     ps = _dev(sink, "sink", (torch.int32,))
     _check("dgw4_hbm_read_probe",
            lib().dgw4_hbm_read_probe(pb, buf.numel(), ps, _stream(buf)))
+
+
+def mfma_probe(iters: int, sink: torch.Tensor) -> float:
+    """Enqueue the whole-chip MFMA throughput probe (a measurement aid: time
+    it with events on the current stream); returns the launch's
+    floating-point operations. ``sink`` device int32, at least one element."""
+    ps = _dev(sink, "sink", (torch.int32,))
+    flops = ctypes.c_double(0.0)
+    _check("dgw4_mfma_probe", lib().dgw4_mfma_probe(int(iters), ps, ctypes.byref(flops),
+                                                    _stream(sink)))
+    return flops.value
 
 
 STAGES = ("align", "gate_up", "down", "combine")

@@ -380,6 +380,13 @@ int dgw4_hbm_read_probe(const void *buf, size_t bytes, uint32_t *sink, void *str
     return from_hip(dgw4::launch_read_probe(buf, bytes, sink, (hipStream_t)stream));
 }
 
+int dgw4_mfma_probe(int iters, uint32_t *sink, double *flops, void *stream)
+{
+    if (iters < 1 || !sink || !flops)
+        return DGW4_ERR_INVALID_ARG;
+    return from_hip(dgw4::launch_mfma_probe(iters, sink, flops, (hipStream_t)stream));
+}
+
 int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
                       const uint16_t *s, const uint16_t *z, int garg, uint16_t *y, void *stream)
 {

@@ -107,6 +107,10 @@ hipError_t sample_scratch(void **ptr);
 // dgw4_hbm_read_probe.
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
 
+// The MFMA throughput probe (see dgw4_mfma_probe); *flops gets the launch's
+// floating-point operations.
+hipError_t launch_mfma_probe(int iters, uint32_t *sink, double *flops, hipStream_t stream);
+
 // y: `halves` (1 or 2) fp16 arrays [T * topk, d] one after the other; each
 // assignment's expert output is their sum.
 hipError_t launch_combine(const uint16_t *y, int halves, const int32_t *topk_ids,
