@@ -78,6 +78,11 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 // a.sorted_ids / a.tile_info unused, one weight matrix (n_w = n_out = N rows),
 // a.out = y fp16 [A, N] in natural column order.
 hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
+
+// The many-row dense linear (linear.hip): whether its LDS and alignment needs
+// hold for a, and its launch (a.A rows in 256-row blocks).
+bool linear_wide_fits(const GemmArgs &a, int g);
+hipError_t launch_linear_wide(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
 
 // Whether alignment and the pair of GEMMs run as one launch (the layer's
