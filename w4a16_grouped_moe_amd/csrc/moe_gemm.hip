@@ -48,14 +48,14 @@
 //   alignment: each workgroup finds its tile's expert and rows from the
 //     expert ids itself (histogram, fixed-order scan, stable ranks in LDS);
 //   gate_up4: H[:, 352 h .. + 352] of the tile; wave w owns pairs 2w and
-//     2w + 1 (16 gate columns and the matching up columns each) and computes
-//     them in two passes over K (11 line steps of 256 each), straight-line,
-//     with the loads of the second pass issued during the end of the first.
-//     The step's activation slice is staged in LDS once for the 11 waves; H
-//     stays in LDS;
+//     2w + 1 (16 gate columns and the matching up columns each) and walks K
+//     in 22 straight-line steps of one group of 128 for all four of its
+//     weight tiles. The step's activation slice is staged in LDS once for the
+//     11 waves; H stays in LDS;
 //   down, split along K: the workgroup's H half times the matching half of
 //     every down row gives an fp16 partial of all 2816 outputs, stored per
-//     assignment; the combine adds the two partials. No workgroup waits for
+//     assignment; the waves share out the 176 row tiles through an LDS
+//     counter; the combine adds the two partials. No workgroup waits for
 //     another.
 // down4 (workgroup = (tile, 1408 output columns), the tile's H rows and the
 // block's scales/zero points staged in LDS once, wave w streaming row tiles
