@@ -66,7 +66,11 @@ def layer_bytes(shape, populated: int) -> dict:
 TRAFFIC_PROFILE = "profiles/layer_kernel_hbm_traffic_stack_skew_wide.md"
 TRAFFIC_SOURCES = ("w4a16_grouped_moe_amd/csrc/moe_gemm.hip",
                    "w4a16_grouped_moe_amd/csrc/gemm_common.hpp",
-                   "w4a16_grouped_moe_amd/csrc/dgw4_internal.hpp")
+                   "w4a16_grouped_moe_amd/csrc/dgw4_internal.hpp",
+                   "w4a16_grouped_moe_amd/csrc/wide_gemm.hpp",
+                   "w4a16_grouped_moe_amd/csrc/chunk_gate_up.hip",
+                   "w4a16_grouped_moe_amd/csrc/chunk_down.hip",
+                   "w4a16_grouped_moe_amd/csrc/align.hip")
 
 
 def gemm_source_hash() -> str:
@@ -79,11 +83,12 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
-def traffic_key(shape, layout: str) -> dict:
+def traffic_key(shape, layout: str, row_block: int) -> dict:
     """What a counter record must have been taken on to describe this run."""
     return {"T": shape.T, "E": shape.E, "topk": shape.topk, "d": shape.d, "m": shape.m,
             "g_gu": shape.g_gu, "g_dn": shape.g_dn,
-            "routing": f"zipf({shape.zipf})" if shape.zipf else "uniform", "layout": layout}
+            "routing": f"zipf({shape.zipf})" if shape.zipf else "uniform", "layout": layout,
+            "row_block": row_block}
 
 
 def measured_traffic(key: dict) -> dict | None:
@@ -137,7 +142,7 @@ def make_layer(torch, dg, shape, l: int, dev, layout: str = "tiled", keep_master
         populated=populated, masters=masters, x_host=x, logits_host=logits)
 
 
-def graph_replay(torch, dg, step, L, R, out, last, ws, dev) -> dict:
+def graph_replay(torch, dg, step, L, R, out, last, ws, dev, rows: str = "auto") -> dict:
     """Capture one sweep of L layer forwards into a HIP graph, replay it R
     times, and compare the last layer's output with an eager forward."""
     stream = torch.cuda.current_stream(dev)
@@ -162,7 +167,8 @@ def graph_replay(torch, dg, step, L, R, out, last, ws, dev) -> dict:
     torch.cuda.synchronize()
     us = np.array([ev[r].elapsed_time(ev[r + 1]) * 1e3 / L for r in range(R)])
     replayed = out.clone()
-    eager = dg.moe_forward(last["x"], last["ids"], last["w"], last["gu"], last["dn"], workspace=ws)
+    eager = dg.moe_forward(last["x"], last["ids"], last["w"], last["gu"], last["dn"], workspace=ws,
+                           rows=rows)
     torch.cuda.synchronize()
     same = bool(torch.equal(replayed.view(torch.int16), eager.view(torch.int16)))
     del g
@@ -391,6 +397,9 @@ def main() -> int:
     ap.add_argument("--weight-layout", default="tiled", choices=["tiled", "canonical"],
                     help="layout of the packed weights the timed steps read (both give "
                          "identical results; the other one is timed in a short pass too)")
+    ap.add_argument("--rows", default="auto", choices=["auto", "tiles", "chunks"],
+                    help="row blocks of the expert GEMMs: the library's choice (default), "
+                         "32-row tiles or 128-row chunks (see DGW4_ROWS_* in include/dgw4.h)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, metavar="MIB", default=0,
                     help="only run a plain device copy of MIB MiB 5 times (the counter "
@@ -436,16 +445,26 @@ def main() -> int:
     log(f"[bench] {L} layers packed on the device in {time.time() - t0:.1f}s "
         f"({sum(x['bytes']['weights'] for x in layers) / 1e9:.2f} GB of packed weights touched)")
 
-    ws = torch.empty(dg.workspace_bytes(shape.T, shape.topk, shape.E, shape.d, shape.m,
-                                        shape.g_gu, shape.g_dn), dtype=torch.uint8, device=dev)
+    # (the workspace depends on the row blocks the library picks, which
+    # depend on the weight layout: size it for both layouts the steps use)
+    ws = torch.empty(max(dg.workspace_bytes(shape.T, shape.topk, shape.E, shape.d, shape.m,
+                                            layers[0][k][3], layers[0][j][3],
+                                            rows=args.rows if k == "gu" else "auto")
+                         for k, j in (("gu", "dn"), ("gu_other", "dn_other"))),
+                     dtype=torch.uint8, device=dev)
+    row_block = dg.row_block(shape.T, shape.topk, shape.E, shape.d, shape.m,
+                             layers[0]["gu"][3], layers[0]["dn"][3], rows=args.rows)
+    log(f"[bench] expert GEMMs on {'128-row chunks' if row_block == 128 else '32-row tiles'}")
     out = torch.empty((shape.T, shape.d), dtype=torch.float16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step(i, events=None, other=False):
         ly = layers[i % L]
         gu, dn = (ly["gu_other"], ly["dn_other"]) if other else (ly["gu"], ly["dn"])
+        # (the other layout's pass takes the library's choice: chunks need
+        # tiled weights)
         dg.moe_forward(ly["x"], ly["ids"], ly["w"], gu, dn, workspace=ws, out=out,
-                       events=events)
+                       events=events, rows="auto" if other else args.rows)
 
     for i in range(args.warmup):
         step(i)
@@ -493,7 +512,7 @@ def main() -> int:
     # The same sweep replayed as one HIP graph (captured once; every replay
     # re-runs alignment and both GEMMs on the device), checked bitwise
     # against the eager result of its last layer.
-    graph = graph_replay(torch, dg, step, L, R, out, layers[L - 1], ws, dev)
+    graph = graph_replay(torch, dg, step, L, R, out, layers[L - 1], ws, dev, args.rows)
 
     # Stage split, in a pass of its own after the timed region: each recorded
     # event adds a few microseconds of dispatch gap, so they stay out of the
@@ -516,7 +535,7 @@ def main() -> int:
     # the two ends only, so the average includes no event's dispatch gap.
     def experts(i):
         ly = layers[i % L]
-        dg.moe_experts(ly["x"], ly["ids"], ly["gu"], ly["dn"], ws)
+        dg.moe_experts(ly["x"], ly["ids"], ly["gu"], ly["dn"], ws, rows=args.rows)
     for i in range(L):
         experts(i)
     e0 = torch.cuda.Event(enable_timing=True)
@@ -540,7 +559,7 @@ def main() -> int:
     def routed(i):
         ly = layers[i % L]
         dg.moe_forward_routed(ly["x"], logits_d[i % L], shape.topk, ly["gu"], ly["dn"],
-                              workspace=ws, out=out)
+                              workspace=ws, out=out, rows=args.rows)
 
     def router_only(i):
         dg.router(logits_d[i % L], shape.topk, rids, rw)
@@ -562,7 +581,7 @@ def main() -> int:
     moved = sum(layers[i % L]["bytes"]["layer"] for i in range(K))
     ms_per_step = total_ms / K
     gbps = moved / (total_ms * 1e-3) / 1e9
-    fused = (shape.d, shape.m, shape.g_gu, shape.g_dn) == (2816, 704, 128, 64)
+    fused = row_block == 32 and (shape.d, shape.m, shape.g_gu, shape.g_dn) == (2816, 704, 128, 64)
     names = ("layer_kernel", "gap", "gap2", "combine") if fused else \
         ("align", "gate_up", "down", "combine")
     stage_us = {n: round(float(stage_ms[:, j].mean() * 1e3), 2) for j, n in enumerate(names)}
@@ -575,7 +594,7 @@ def main() -> int:
 
     probe = read_probe(torch, dg, dev)
     probe["pct_of_probe"] = round(100 * gbps / probe["gbps"], 2)
-    traffic = measured_traffic(traffic_key(shape, args.weight_layout))
+    traffic = measured_traffic(traffic_key(shape, args.weight_layout, row_block))
     pages_gbps = layers[0]["bytes"]["layer"] / (GB10_LAYER_MS * 1e-3) / 1e9
     result = {
         "metric": METRIC,
@@ -605,6 +624,7 @@ def main() -> int:
             "d": shape.d,
             "m": shape.m,
             "weight_layout": args.weight_layout,
+            "row_block": row_block,
         },
         "us_per_layer": round(ms_per_step * 1e3, 2),
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -623,7 +643,9 @@ def main() -> int:
             "kernel": (f"layer_kernel<{str(args.weight_layout == 'tiled').lower()}> (alignment, "
                        f"gate_up + GELU(tanh) gate and down in one launch, layer shape, "
                        f"{args.weight_layout} weights)" if fused else
-                       f"align, gate_up and down launches together ({args.weight_layout} weights)"),
+                       (f"align (128-row chunks), chunk_gate_up_kernel and chunk_down_kernel "
+                        f"together ({args.weight_layout} weights)" if row_block == 128 else
+                        f"align, gate_up and down launches together ({args.weight_layout} weights)")),
             "bound": "hbm",
             "achieved": round(kern_gbps, 1),
             "peak": HBM_PEAK_GBPS,

@@ -71,6 +71,27 @@ typedef enum {
 /* Or-ed into a GEMM's group-size argument: that matrix is in the tiled layout. */
 #define DGW4_WEIGHTS_TILED 0x10000
 
+/*
+ * Or-ed into the layer's gate_up group-size argument (gu_g of
+ * dgw4_moe_forward, _timed, _routed and dgw4_moe_experts, the workspace
+ * query included): the row blocks the expert GEMMs run on.
+ *   DGW4_ROWS_TILES   each expert's sorted assignments padded to 32-row
+ *                     tiles; a workgroup per tile (and column block) reads
+ *                     the expert's weights, so an expert's weights are read
+ *                     once per tile. Fastest when experts hold few rows.
+ *   DGW4_ROWS_CHUNKS  padded to 128-row chunks; the weights are formed once
+ *                     per chunk and feed all its rows. Fastest when experts
+ *                     hold many rows. Exists for d = 2816 at gate_up g = 128
+ *                     and m = 704 at down g = 64 (else DGW4_ERR_UNSUPPORTED).
+ * Neither (the default): chunks when they exist for the shape and the
+ * experts hold at least 48 assignments each on average (T * topk >= 48 E),
+ * else tiles. Both bits: DGW4_ERR_INVALID_ARG. The two give the same results
+ * up to rounding: tiles apply each group's scale to an fp32 partial, chunks
+ * round each dequantised weight (q - z) * s to fp16 once.
+ */
+#define DGW4_ROWS_TILES 0x20000
+#define DGW4_ROWS_CHUNKS 0x40000
+
 /* Human-readable name of a status code (static storage). */
 DGW4_API const char *dgw4_status_string(int status);
 
@@ -191,9 +212,11 @@ DGW4_API int dgw4_router(const float *logits, int T, int E, int topk, int32_t *i
  *            w[t,k] * down_e( gelu_tanh(gate_e(x[t])) * up_e(x[t] ) ),  e = ids[t,k]
  * with expert weights dequantised as w = (q - z) * s. Accumulation is fp32;
  * the gated intermediate and each expert output are rounded to fp16 once
- * (at the layer's shape, d = 2816, m = 704, gate_up g = 128, down g = 64,
- * each expert output is kept as two fp16 partials, one per half of down's
- * contraction, added in fp32 by the combine), and the combine sums
+ * (on 32-row tiles at the layer's shape, d = 2816, m = 704, gate_up g = 128,
+ * down g = 64, each expert output is kept as two fp16 partials, one per half
+ * of down's contraction, added in fp32 by the combine; on 128-row chunks
+ * each dequantised weight is rounded to fp16 once, see DGW4_ROWS_CHUNKS),
+ * and the combine sums
  * w[t,k] * output in ascending k in fp32 without atomics, then rounds once
  * to fp16. No workgroup waits for another and nothing depends on timing:
  * repeated calls on the same inputs give bit-identical results.
@@ -209,7 +232,8 @@ DGW4_API int dgw4_router(const float *logits, int T, int E, int topk, int32_t *i
  *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED), each or-ed
  *              with DGW4_WEIGHTS_TILED when that stack's q is in the tiled
  *              layout (same results; the layer's shape runs fastest with both
- *              tiled). Other bits: DGW4_ERR_INVALID_ARG.
+ *              tiled); gu_g may also carry DGW4_ROWS_TILES or
+ *              DGW4_ROWS_CHUNKS. Other bits: DGW4_ERR_INVALID_ARG.
  *   workspace  device scratch of at least *ws_bytes bytes, 256-byte aligned.
  *              If workspace is NULL, the required size is written to
  *              *ws_bytes and nothing is launched. Contents on entry are
@@ -224,15 +248,25 @@ DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const 
                      void *workspace, size_t *ws_bytes, uint16_t *out, void *stream);
 
 /*
+ * dgw4_moe_row_block — the row blocks dgw4_moe_forward runs its expert GEMMs
+ * on for these arguments (gu_g with its DGW4_ROWS_* and DGW4_WEIGHTS_TILED
+ * bits, dn_g with its layout bit): 32 (tiles) or 128 (chunks). Host only,
+ * launches nothing. Returns the negated status for arguments the forward's
+ * workspace query rejects (e.g. -DGW4_ERR_UNSUPPORTED for chunks asked for
+ * where they do not exist).
+ */
+DGW4_API int dgw4_moe_row_block(int T, int topk, int E, int d, int m, int gu_g, int dn_g);
+
+/*
  * dgw4_moe_forward_timed — dgw4_moe_forward with stage events, for per-kernel
  * timing of the same launch sequence (same kernels, same arguments, same
  * results). events is an array of n_events = 5 caller-created hipEvent_t
  * handles (passed as void*); they are recorded on `stream` before the first
  * kernel and after each of the four stages (align, gate_up, down, combine).
  * Elapsed time between consecutive events is the duration of one stage.
- * Where alignment, gate_up and down run as one launch (the layer's shape:
- * d = 2816, m = 704, gate_up g = 128, down g = 64, both stacks in the same
- * layout), events 1, 2 and 3 are all recorded after that launch, so the
+ * Where alignment, gate_up and down run as one launch (32-row tiles at the
+ * layer's shape: d = 2816, m = 704, gate_up g = 128, down g = 64, both
+ * stacks in the same layout), events 1, 2 and 3 are all recorded after that launch, so the
  * first stage brackets it and the next two bracket no kernel. events == NULL
  * behaves exactly like dgw4_moe_forward; any other n_events is
  * DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL) records

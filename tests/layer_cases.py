@@ -101,8 +101,9 @@ def custom_shape(name, E, topk, T, d, m, g_gu=128, g_dn=64, zipf=None, index=90)
                       zipf=zipf)
 
 
-def gpu_forward(L: Layer, workspace=None) -> np.ndarray:
-    out = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=workspace)
+def gpu_forward(L: Layer, workspace=None, rows: str = "auto") -> np.ndarray:
+    out = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=workspace,
+                         rows=rows)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 

@@ -190,7 +190,7 @@ def test_layout_flag_bits():
     assert tiled == 0x10000
     # the flag is accepted on either stack; any other high bit is not
     assert _fwd(T=0, x=None, ids=None, w=None, out=None, gg=128 | tiled, dg=64 | tiled) == B.OK
-    assert _fwd(gg=128 | 0x20000) == B.ERR_INVALID_ARG
+    assert _fwd(gg=128 | 0x80000) == B.ERR_INVALID_ARG
     assert _fwd(dg=64 | (1 << 30)) == B.ERR_INVALID_ARG
     assert _fwd(gg=-128) == B.ERR_INVALID_ARG
     n = dg.workspace_bytes(256, 8, 128, 2816, 704, 128 | tiled, 64 | tiled)
@@ -199,6 +199,50 @@ def test_layout_flag_bits():
     p = 1 << 12
     assert f(p, 4, 256, 64, p, p, p, 64 | 0x40000, p, None) == B.ERR_INVALID_ARG
     assert f(None, 0, 256, 64, None, None, None, 64 | tiled, None, None) == B.OK
+
+
+def test_rows_flags():
+    # the row-block choice rides on gate_up's group argument; every call here
+    # is a workspace query or fails validation, so nothing is launched
+    assert (B.ROWS_TILES, B.ROWS_CHUNKS) == (0x20000, 0x40000)
+    t = B.WEIGHTS_TILED
+    both = B.ROWS_TILES | B.ROWS_CHUNKS
+    layer = dict(ws=None, T=4, topk=2, E=8, d=2816, m=704)
+    assert _fwd(ws=None, gg=128 | both) == B.ERR_INVALID_ARG
+    assert _fwd(ws=None, dg=64 | B.ROWS_CHUNKS) == B.ERR_INVALID_ARG     # not on down's
+    # chunks exist for d = 2816 at g = 128 and m = 704 at g = 64, both stacks
+    # tiled
+    assert _fwd(ws=None, gg=128 | t | B.ROWS_CHUNKS, dg=64 | t) == B.ERR_UNSUPPORTED
+    assert _fwd(**layer, gg=64 | t | B.ROWS_CHUNKS, dg=64 | t) == B.ERR_UNSUPPORTED
+    assert _fwd(**layer, gg=128 | B.ROWS_CHUNKS, dg=64) == B.ERR_UNSUPPORTED
+    assert _fwd(**layer, gg=128 | t | B.ROWS_CHUNKS, dg=64) == B.ERR_UNSUPPORTED
+    assert _fwd(ws=None, gg=128 | B.ROWS_TILES) == B.OK
+    assert _fwd(**layer, gg=128 | t | B.ROWS_CHUNKS, dg=64 | t) == B.OK
+    # workspace: tiles at the layer's shape keep two Y partials; chunks keep
+    # H for 128-row padding and one Y
+    for T in (256, 1024):
+        A = T * 8
+        tiles = dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t, rows="tiles")
+        chunks = dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t, rows="chunks")
+        t_data = (A + 128 * 31) * 704 * 2 + 2 * A * 2816 * 2
+        c_data = (A + 128 * 127) * 704 * 2 + A * 2816 * 2
+        assert t_data <= tiles < t_data + 256 * 1024
+        assert c_data <= chunks < c_data + 256 * 1024
+        # the library's choice: chunks from 48 assignments per expert on
+        # average with tiled weights, tiles otherwise
+        auto = dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t)
+        assert auto == (chunks if A >= 48 * 128 else tiles)
+        assert dg.workspace_bytes(T, 8, 128, 2816, 704) == tiles
+    with pytest.raises(ValueError):
+        dg.workspace_bytes(256, 8, 128, 2816, 704, rows="rows")
+    # the row-block query agrees with the workspace sizes above
+    assert dg.row_block(1024, 8, 128, 2816, 704, 128 | t, 64 | t) == 128
+    assert dg.row_block(256, 8, 128, 2816, 704, 128 | t, 64 | t) == 32
+    assert dg.row_block(1024, 8, 128, 2816, 704) == 32                  # canonical weights
+    assert dg.row_block(256, 8, 128, 2816, 704, 128 | t, 64 | t, rows="chunks") == 128
+    assert dg.row_block(1024, 8, 128, 2816, 704, 128 | t, 64 | t, rows="tiles") == 32
+    assert dg.lib().dgw4_moe_row_block(4, 2, 8, 512, 192, 128 | B.ROWS_CHUNKS, 64) == -B.ERR_UNSUPPORTED
+    assert dg.lib().dgw4_moe_row_block(4, 9, 8, 512, 192, 128, 64) == -B.ERR_INVALID_ARG
 
 
 def test_sample_noalloc_rejects():

@@ -48,8 +48,8 @@ def test_stack_layer_audit(layer):
         host[name] = (hq, hs, hz, g)
     del gw, dw
     sh = shape
-    ws = torch.empty(dg.workspace_bytes(sh.T, sh.topk, sh.E, sh.d, sh.m), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.empty(dg.workspace_bytes(sh.T, sh.topk, sh.E, sh.d, sh.m, ly["gu"][3], ly["dn"][3]),
+                     dtype=torch.uint8, device=dev)
     out = torch.empty((sh.T, sh.d), dtype=torch.float16, device=dev)
     dg.moe_forward(ly["x"], ly["ids"], ly["w"], ly["gu"], ly["dn"], workspace=ws, out=out)
     torch.cuda.synchronize()

@@ -107,9 +107,9 @@ def test_forward_tiled_full_deterministic_100():
     # the benchmarked configuration: tiled weights, the one-launch layer kernel
     L = lc.cached("full")
     sh = L.shape
-    ws = torch.empty(dg.workspace_bytes(sh.T, sh.topk, sh.E, sh.d, sh.m), dtype=torch.uint8,
-                     device="cuda")
     gu, dn = dg.pack_tiled(L.gu_dev), dg.pack_tiled(L.dn_dev)
+    ws = torch.empty(dg.workspace_bytes(sh.T, sh.topk, sh.E, sh.d, sh.m, gu[3], dn[3]),
+                     dtype=torch.uint8, device="cuda")
     first = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, workspace=ws).clone()
     bad = 0
     for i in range(100):

@@ -17,10 +17,13 @@ from .binding import (  # noqa: F401
     moe_forward_routed,
     pack_tiled,
     WEIGHTS_TILED,
+    ROWS_TILES,
+    ROWS_CHUNKS,
     quantize_rtn,
     status_string,
     version,
     workspace_bytes,
+    row_block,
     w4a16_linear,
     sample,
     sample_noalloc,

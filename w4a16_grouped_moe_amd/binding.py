@@ -54,6 +54,8 @@ def lib():
         L.dgw4_align_capacity.argtypes = [I, I, I, I]
         L.dgw4_align.restype = I
         L.dgw4_align.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
+        L.dgw4_moe_row_block.restype = I
+        L.dgw4_moe_row_block.argtypes = [I, I, I, I, I, I, I]
         L.dgw4_moe_forward.restype = I
         L.dgw4_moe_forward.argtypes = [P, P, P, I, I, I, I, I,
                                        P, P, P, I, P, P, P, I,
@@ -146,8 +148,21 @@ def quantize_rtn(w: torch.Tensor, g: int):
 WEIGHTS_TILED = 0x10000
 
 
+# Or-ed into the layer's gate_up group size (include/dgw4.h): the expert
+# GEMMs' row blocks, 32-row tiles or 128-row chunks.
+ROWS_TILES = 0x20000
+ROWS_CHUNKS = 0x40000
+_ROWS = {"auto": 0, "tiles": ROWS_TILES, "chunks": ROWS_CHUNKS}
+
+
 def _group(g: int) -> int:
     return g & 0xFFFF
+
+
+def _rows_flag(rows: str) -> int:
+    if rows not in _ROWS:
+        raise ValueError(f"rows must be one of {sorted(_ROWS)}, not {rows!r}")
+    return _ROWS[rows]
 
 
 def pack_tiled(w: tuple) -> tuple:
@@ -298,13 +313,26 @@ def align(topk_ids: torch.Tensor, E: int, block_m: int = BLOCK_M) -> dict:
 
 
 def workspace_bytes(T: int, topk: int, E: int, d: int, m: int, gu_g: int = 128,
-                    dn_g: int = 64) -> int:
-    """Device workspace dgw4_moe_forward needs for this shape (host-only query)."""
+                    dn_g: int = 64, rows: str = "auto") -> int:
+    """Device workspace dgw4_moe_forward needs for this shape and row-block
+    choice (host-only query)."""
     n = ctypes.c_size_t(0)
     _check("dgw4_moe_forward(query)", lib().dgw4_moe_forward(
-        None, None, None, T, topk, E, d, m, None, None, None, gu_g, None, None, None, dn_g,
+        None, None, None, T, topk, E, d, m, None, None, None, gu_g | _rows_flag(rows), None,
+        None, None, dn_g,
         None, ctypes.byref(n), None, None))
     return int(n.value)
+
+
+def row_block(T: int, topk: int, E: int, d: int, m: int, gu_g: int = 128, dn_g: int = 64,
+              rows: str = "auto") -> int:
+    """The row blocks moe_forward runs its expert GEMMs on for these
+    arguments (gu_g / dn_g with their layout bits): 32 (tiles) or 128
+    (chunks). Host-only query."""
+    r = lib().dgw4_moe_row_block(T, topk, E, d, m, gu_g | _rows_flag(rows), dn_g)
+    if r < 0:
+        _check("dgw4_moe_row_block", -r)
+    return r
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor) -> None:
@@ -333,7 +361,7 @@ STAGES = ("align", "gate_up", "down", "combine")
 
 def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
                 gu: tuple, dn: tuple, workspace: torch.Tensor | None = None,
-                out: torch.Tensor | None = None, events=None) -> torch.Tensor:
+                out: torch.Tensor | None = None, events=None, rows: str = "auto") -> torch.Tensor:
     """One routed-expert layer.
 
     x fp16 [T, d]; topk_ids int32 [T, topk]; topk_w fp32 [T, topk];
@@ -344,8 +372,11 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
     allocated here when not given; pass one to avoid allocation per call.
     ``events``: optional list of 5 torch.cuda.Event(enable_timing=True),
     recorded on the current stream before the alignment kernel and after each
-    of the four kernels (see STAGES)."""
+    of the four kernels (see STAGES). ``rows``: "auto", "tiles" (32-row
+    tiles) or "chunks" (128-row chunks), see DGW4_ROWS_TILES /
+    DGW4_ROWS_CHUNKS in include/dgw4.h."""
     gq, gs, gz, gg = gu
+    gg |= _rows_flag(rows)
     dq, ds, dz, dg = dn
     T, d = x.shape
     topk = topk_ids.shape[1]
@@ -392,11 +423,12 @@ def moe_forward(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
 
 
 def moe_experts(x: torch.Tensor, topk_ids: torch.Tensor, gu: tuple, dn: tuple,
-                workspace: torch.Tensor) -> None:
+                workspace: torch.Tensor, rows: str = "auto") -> None:
     """The expert stages of moe_forward alone (alignment, gate_up, down; no
     combine), leaving the expert outputs in ``workspace``: a measurement aid
     for timing those kernels back to back (see dgw4_moe_experts)."""
     gq, gs, gz, gg = gu
+    gg |= _rows_flag(rows)
     dq, ds, dz, dg = dn
     T, d = x.shape
     topk = topk_ids.shape[1]
@@ -416,10 +448,11 @@ def moe_experts(x: torch.Tensor, topk_ids: torch.Tensor, gu: tuple, dn: tuple,
 
 def moe_forward_routed(x: torch.Tensor, router_logits: torch.Tensor, topk: int, gu: tuple,
                        dn: tuple, workspace: torch.Tensor | None = None,
-                       out: torch.Tensor | None = None) -> torch.Tensor:
+                       out: torch.Tensor | None = None, rows: str = "auto") -> torch.Tensor:
     """One routed-expert layer from router logits fp32 [T, E]: the router
     (dgw4_router), then the layer, in one C-ABI call (dgw4_moe_forward_routed)."""
     gq, gs, gz, gg = gu
+    gg |= _rows_flag(rows)
     dq, ds, dz, dg = dn
     T, d = x.shape
     E = gq.shape[0]

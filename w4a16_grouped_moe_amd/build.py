@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdgw4.so")
 
-SOURCES = ["quantize.hip", "router.hip", "align.hip", "moe_gemm.hip", "linear.hip", "combine.hip", "probe.hip", "sampler.hip", "dgw4_api.cpp"]
+SOURCES = ["quantize.hip", "router.hip", "align.hip", "moe_gemm.hip", "many_rows.hip", "chunk_gate_up.hip", "chunk_down.hip", "combine.hip", "probe.hip", "sampler.hip", "dgw4_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -31,6 +31,21 @@ bool split_group(int arg, int &g, int &tiled)
     return true;
 }
 
+// The layer's row-block choice carried by the gate_up group argument:
+// 0 (the library picks), DGW4_ROWS_TILES or DGW4_ROWS_CHUNKS; the bits are
+// removed from arg. False for both bits together.
+bool split_rows(int &arg, int &rows)
+{
+    rows = arg & (DGW4_ROWS_TILES | DGW4_ROWS_CHUNKS);
+    arg &= ~(DGW4_ROWS_TILES | DGW4_ROWS_CHUNKS);
+    return rows != (DGW4_ROWS_TILES | DGW4_ROWS_CHUNKS);
+}
+
+// With no choice given, the layer runs on 128-row chunks once the experts
+// hold this many assignments each on average (and the chunk GEMMs exist for
+// the shape), else on 32-row tiles.
+constexpr long long kChunkMinMeanRows = 48;
+
 bool overlap(const void *a, const void *b, size_t bytes)
 {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -47,17 +62,18 @@ int from_hip(hipError_t e)
     return DGW4_ERR_HIP;
 }
 
-// Workspace of one forward call: alignment buffers, the gated intermediate H
-// (fp16, one row per padded assignment) and the per-assignment expert outputs
-// Y (fp16, one row per flat assignment id; two such arrays, the partials of
-// the two halves of down's contraction, at the layer's shape). The layer
-// kernel aligns inside its workgroups and keeps H in LDS, so at the layer's
-// shape only Y is used.
+// Workspace of one forward call: alignment buffers (for block_m-row
+// blocks), the gated intermediate H (fp16, one row per padded assignment) and
+// the per-assignment expert outputs Y (fp16, one row per flat assignment id;
+// `halves` such arrays). On 32-row tiles at the layer's shape, the layer
+// kernel aligns inside its workgroups, keeps H in LDS and writes two Y
+// arrays, the partials of the two halves of down's contraction; on 128-row
+// chunks the alignment, H and one Y are used.
 struct Layout {
     size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, rids, rw, total;
 };
 
-Layout layout(long long A, int T, int E, int d, int m, long long cap)
+Layout layout(long long A, int T, int E, int d, int m, long long cap, int block_m, int halves)
 {
     Layout L{};
     size_t off = 0;
@@ -69,11 +85,11 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap)
     L.counts = take(sizeof(int32_t) * (size_t)E);
     L.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
     L.num_padded = take(sizeof(int32_t));
-    L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / dgw4::kBlockM));
-    L.tile_info = take(sizeof(int2) * (size_t)(cap / dgw4::kBlockM));
+    L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / block_m));
+    L.tile_info = take(sizeof(int2) * (size_t)(cap / block_m));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
-    L.y = take(2 * sizeof(uint16_t) * (size_t)A * (size_t)d);
+    L.y = take((size_t)halves * sizeof(uint16_t) * (size_t)A * (size_t)d);
     L.rids = take(sizeof(int32_t) * (size_t)A);       // the router's output (routed forward)
     L.rw = take(sizeof(float) * (size_t)A);
     L.total = off;
@@ -146,6 +162,22 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
 
 namespace {
 
+// The row blocks of the layer's expert GEMMs (kBlockM or kChunkM) for the
+// GEMMs' shapes (gu, dn without buffers) and the caller's choice; -1 for
+// chunks asked for where they do not exist.
+int pick_rows(dgw4::GemmArgs gu, int gu_g, dgw4::GemmArgs dn, int dn_g, int rows, int E,
+              size_t cap128)
+{
+    gu.max_tiles = (int)(cap128 / dgw4::kChunkM);
+    dn.max_tiles = gu.max_tiles;
+    dn.a_rows = (int)cap128;
+    const bool chunk_ok = dgw4::chunk_gemms_fit(gu, gu_g, dn, dn_g);
+    if (rows == DGW4_ROWS_CHUNKS)
+        return chunk_ok ? dgw4::kChunkM : -1;
+    const bool chunks = rows == 0 && chunk_ok && (long long)gu.A >= kChunkMinMeanRows * E;
+    return chunks ? dgw4::kChunkM : dgw4::kBlockM;
+}
+
 // The forward (with_combine) or its expert stages alone; events (5 or null)
 // are recorded before the first kernel and after each stage: alignment,
 // gate_up, down, combine. At the layer's shape the first three are one
@@ -157,8 +189,9 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
                      uint16_t *out, void *stream, void *const *events, int n_events,
                      bool with_combine, const float *router_logits = nullptr)
 {
-    int gu_g = 0, dn_g = 0, gu_tiled = 0, dn_tiled = 0;
-    if (!split_group(gu_garg, gu_g, gu_tiled) || !split_group(dn_garg, dn_g, dn_tiled))
+    int gu_g = 0, dn_g = 0, gu_tiled = 0, dn_tiled = 0, rows = 0;
+    if (!split_rows(gu_garg, rows) || !split_group(gu_garg, gu_g, gu_tiled) ||
+        !split_group(dn_garg, dn_g, dn_tiled))
         return DGW4_ERR_INVALID_ARG;
     if (events && n_events != 5)
         return DGW4_ERR_INVALID_ARG;
@@ -177,18 +210,48 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     if (d % gu_g != 0 || m % dn_g != 0)
         return DGW4_ERR_INVALID_ARG;
     const long long A = (long long)T * topk;
-    const size_t cap = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
-    if (cap == 0 || A > INT_MAX)
+    const size_t cap32 = dgw4_align_capacity(T, topk, E, dgw4::kBlockM);
+    const size_t cap128 = dgw4_align_capacity(T, topk, E, dgw4::kChunkM);
+    if (cap32 == 0 || cap128 == 0 || A > INT_MAX)
         return DGW4_ERR_INVALID_ARG;
     if (dgw4::gemm_lds_bytes(true, d, gu_g) > kMaxGemmLds ||
         dgw4::gemm_lds_bytes(false, m, dn_g) > kMaxGemmLds || m > dgw4::down_max_k() ||
         d / gu_g > dgw4::gate_up_max_groups())
         return DGW4_ERR_UNSUPPORTED;
+
+    // the GEMMs' shapes; the buffers are filled in below
+    dgw4::GemmArgs gu{};
+    gu.topk = topk;
+    gu.A = (int)A;
+    dgw4::GemmArgs dn = gu;
+    gu.a_rows = T;
+    gu.K = d;
+    gu.n_w = 2 * m;
+    gu.n_out = m;
+    gu.tiled = gu_tiled;
+    dn.K = m;
+    dn.n_w = d;
+    dn.n_out = d;
+    dn.tiled = dn_tiled;
+
+    // the row blocks: 128-row chunks where asked for or where the experts hold
+    // many rows each (and the chunk GEMMs exist for the shape), else 32-row
+    // tiles
+    const int pick = pick_rows(gu, gu_g, dn, dn_g, rows, E, cap128);
+    if (pick < 0)
+        return DGW4_ERR_UNSUPPORTED;
+    const bool chunks = pick == dgw4::kChunkM;
+    const int block_m = chunks ? dgw4::kChunkM : dgw4::kBlockM;
+    const size_t cap = chunks ? cap128 : cap32;
+    gu.max_tiles = (int)(cap / block_m);
+    dn.max_tiles = gu.max_tiles;
+    dn.a_rows = (int)cap;
     // the GEMMs address x, H, Y and one expert's packed weights with 32-bit offsets
     if ((long long)T * d * 2 >= (1LL << 31) || (long long)cap * m * 2 >= (1LL << 31) ||
         (long long)2 * m * d / 2 >= (1LL << 31))
         return DGW4_ERR_UNSUPPORTED;
-    const Layout L = layout(A, T, E, d, m, (long long)cap);
+    const bool fused = !chunks && dgw4::layer_fused(gu, gu_g, dn, dn_g, E);
+    const Layout L = layout(A, T, E, d, m, (long long)cap, block_m, fused ? 2 : 1);
     if (!workspace) {
         *ws_bytes = L.total;
         return DGW4_OK;
@@ -225,35 +288,18 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
 
-    dgw4::GemmArgs gu{};
-    gu.sorted_ids = sorted_ids;
-    gu.tile_info = tile_info;
-    gu.topk = topk;
-    gu.A = (int)A;
-    gu.max_tiles = (int)(cap / dgw4::kBlockM);
-    dgw4::GemmArgs dn = gu;
-
+    gu.sorted_ids = dn.sorted_ids = sorted_ids;
+    gu.tile_info = dn.tile_info = tile_info;
     gu.a_src = x;
-    gu.a_rows = T;
     gu.q = gu_q;
     gu.s = gu_s;
     gu.z = gu_z;
-    gu.K = d;
-    gu.n_w = 2 * m;
-    gu.n_out = m;
     gu.out = h;
-    gu.tiled = gu_tiled;
-
     dn.a_src = h;
-    dn.a_rows = (int)cap;
     dn.q = dn_q;
     dn.s = dn_s;
     dn.z = dn_z;
-    dn.K = m;
-    dn.n_w = d;
-    dn.n_out = d;
     dn.out = y;
-    dn.tiled = dn_tiled;
 
     hipError_t err = mark(0);
     if (err != hipSuccess)
@@ -267,7 +313,6 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
         topk_ids = rids;
         topk_w = rw;
     }
-    const bool fused = dgw4::layer_fused(gu, gu_g, dn, dn_g, E);
     if (fused) {
         // alignment, gate_up and down in one launch: marks 1, 2 and 3 all follow it
         if ((err = dgw4::launch_layer(gu, dn, topk_ids, E, st)) != hipSuccess ||
@@ -275,14 +320,18 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
             (err = mark(3)) != hipSuccess)
             return from_hip(err);
     } else {
-        if ((err = dgw4::launch_align(topk_ids, (int)A, E, dgw4::kBlockM, (long long)cap, counts,
+        if ((err = dgw4::launch_align(topk_ids, (int)A, E, block_m, (long long)cap, counts,
                                       offsets, sorted_ids, tile_expert, num_padded, tile_info,
                                       st)) != hipSuccess ||
             (err = mark(1)) != hipSuccess)
             return from_hip(err);
-        if ((err = dgw4::launch_gate_up(gu, gu_g, st)) != hipSuccess || (err = mark(2)) != hipSuccess)
+        if ((err = chunks ? dgw4::launch_chunk_gate_up(gu, st) : dgw4::launch_gate_up(gu, gu_g, st)) !=
+                hipSuccess ||
+            (err = mark(2)) != hipSuccess)
             return from_hip(err);
-        if ((err = dgw4::launch_down(dn, dn_g, st)) != hipSuccess || (err = mark(3)) != hipSuccess)
+        if ((err = chunks ? dgw4::launch_chunk_down(dn, st) : dgw4::launch_down(dn, dn_g, st)) !=
+                hipSuccess ||
+            (err = mark(3)) != hipSuccess)
             return from_hip(err);
     }
     if (!with_combine)
@@ -295,6 +344,36 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
 }
 
 }  // namespace
+
+int dgw4_moe_row_block(int T, int topk, int E, int d, int m, int gu_g, int dn_g)
+{
+    size_t ws = 0;
+    // the forward's own checks (a workspace query launches nothing)
+    const int st = moe_forward_impl(nullptr, nullptr, nullptr, T, topk, E, d, m, nullptr, nullptr,
+                                    nullptr, gu_g, nullptr, nullptr, nullptr, dn_g, nullptr, &ws,
+                                    nullptr, nullptr, nullptr, 0, true);
+    if (st != DGW4_OK)
+        return -st;
+    int gg = 0, rows = 0, g = 0, gt = 0, dgr = 0, dt = 0;
+    gg = gu_g;
+    split_rows(gg, rows);
+    split_group(gg, g, gt);
+    split_group(dn_g, dgr, dt);
+    dgw4::GemmArgs gu{};
+    gu.topk = topk;
+    gu.A = T * topk;
+    dgw4::GemmArgs dn = gu;
+    gu.a_rows = T;
+    gu.K = d;
+    gu.n_w = 2 * m;
+    gu.n_out = m;
+    gu.tiled = gt;
+    dn.K = m;
+    dn.n_w = d;
+    dn.n_out = d;
+    dn.tiled = dt;
+    return pick_rows(gu, g, dn, dgr, rows, E, dgw4_align_capacity(T, topk, E, dgw4::kChunkM));
+}
 
 int dgw4_moe_forward_timed(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                            int T, int topk, int E, int d, int m, const uint8_t *gu_q,

@@ -11,6 +11,10 @@ namespace dgw4 {
 // (two 16-row MFMA blocks).
 constexpr int kBlockM = 32;
 
+// Rows of one chunk of the many-row expert GEMMs: an expert's sorted
+// assignments padded to a multiple of 128 and taken 128 at a time.
+constexpr int kChunkM = 128;
+
 // Largest expert count the single-workgroup alignment kernel supports.
 constexpr int kMaxExperts = 1024;
 
@@ -79,11 +83,21 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 // a.out = y fp16 [A, N] in natural column order.
 hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
 
-// The many-row dense linear (linear.hip): whether its LDS and alignment needs
+// The many-row dense linear (many_rows.hip): whether its LDS and alignment needs
 // hold for a, and its launch (a.A rows in 256-row blocks).
 bool linear_wide_fits(const GemmArgs &a, int g);
 hipError_t launch_linear_wide(const GemmArgs &a, int g, hipStream_t stream);
 hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream);
+
+// The many-row expert GEMMs (many_rows.hip), over 128-row chunks (the
+// alignment with block_m = kChunkM: sorted_ids / tile_info per chunk):
+// whether they exist for these shapes and buffers, and their launches.
+// gate_up writes H fp16 [max_tiles * kChunkM, m] in natural column order
+// (dn.a_src, dn.a_rows = max_tiles * kChunkM); down writes Y fp16 [A, d],
+// one row per assignment (the combine's halves = 1).
+bool chunk_gemms_fit(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g);
+hipError_t launch_chunk_gate_up(const GemmArgs &gu, hipStream_t stream);
+hipError_t launch_chunk_down(const GemmArgs &dn, hipStream_t stream);
 
 // Whether alignment and the pair of GEMMs run as one launch (the layer's
 // shape), and that launch. It reads the expert ids itself (gu.sorted_ids and
