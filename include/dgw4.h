@@ -42,7 +42,9 @@
  * s and z keep their layout. dgw4_pack_tiled converts; the GEMM entry points
  * take a matrix in that layout when its group-size argument carries
  * DGW4_WEIGHTS_TILED (g | DGW4_WEIGHTS_TILED). Results are bit-identical to
- * those of the canonical layout.
+ * those of the canonical layout on the same kernels; the layer's 128-row
+ * chunks (DGW4_ROWS_CHUNKS, the library's choice for tiled weights when the
+ * experts hold many rows) take tiled weights only.
  */
 #ifndef DGW4_H
 #define DGW4_H
@@ -231,8 +233,9 @@ DGW4_API int dgw4_router(const float *logits, int T, int E, int topk, int32_t *i
  *              (x, the six pack pointers: 16-byte aligned; out: 8-byte aligned)
  *   gu_g, dn_g 64 or 128 each (others: DGW4_ERR_UNSUPPORTED), each or-ed
  *              with DGW4_WEIGHTS_TILED when that stack's q is in the tiled
- *              layout (same results; the layer's shape runs fastest with both
- *              tiled); gu_g may also carry DGW4_ROWS_TILES or
+ *              layout (same results on the same row blocks; the layer's
+ *              shape runs fastest with both tiled, and only then can it take
+ *              128-row chunks); gu_g may also carry DGW4_ROWS_TILES or
  *              DGW4_ROWS_CHUNKS. Other bits: DGW4_ERR_INVALID_ARG.
  *   workspace  device scratch of at least *ws_bytes bytes, 256-byte aligned.
  *              If workspace is NULL, the required size is written to

@@ -52,10 +52,14 @@ def test_pack_tiled_empty_stack():
 
 
 def _forward_pair(L, gu_t=True, dn_t=True, workspace=None):
+    # both layouts on 32-row tiles, where they give bit-identical results (at
+    # many rows per expert the library's choice for tiled weights is 128-row
+    # chunks, which round differently; the chunk tests cover those)
     gu = _tiled(L.gu_dev) if gu_t else L.gu_dev
     dn = _tiled(L.dn_dev) if dn_t else L.dn_dev
-    canon = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=workspace).clone()
-    tiled = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, workspace=workspace)
+    canon = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, L.gu_dev, L.dn_dev, workspace=workspace,
+                           rows="tiles").clone()
+    tiled = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, workspace=workspace, rows="tiles")
     torch.cuda.synchronize()
     assert torch.equal(tiled.view(torch.int16), canon.view(torch.int16)), "tiled != canonical"
     return tiled.cpu().numpy()

@@ -11,7 +11,7 @@
 //   2. offset of e = sum of the block-padded counts of the experts below e,
 //      total = the sum over all experts (block reductions in a fixed order);
 //   3. stable compaction of the flat ids i with ids[i] == e: thread t holds
-//      ids c0 + 8t .. c0 + 8t + 7 of a 2048-id chunk, an exclusive block scan
+//      ids c0 + 8t .. c0 + 8t + 7 of an 8192-id chunk, an exclusive block scan
 //      of the per-thread match counts gives each thread its first slot, and
 //      the matches are written in ascending i;
 //   4. e writes its pad entries, counts/offsets and its tile map entries
@@ -27,7 +27,7 @@
 namespace dgw4 {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kPer = 8;                       // ids per thread per chunk
 constexpr int kChunk = kThreads * kPer;       // ids per chunk
