@@ -63,7 +63,7 @@ def layer_bytes(shape, populated: int) -> dict:
     )
 
 
-TRAFFIC_PROFILE = "profiles/layer_kernel_hbm_traffic_stack_skew_wide.md"
+TRAFFIC_PROFILE = "profiles/expert_stages_hbm_traffic_stack_skew_wide.md"
 TRAFFIC_SOURCES = ("w4a16_grouped_moe_amd/csrc/moe_gemm.hip",
                    "w4a16_grouped_moe_amd/csrc/gemm_common.hpp",
                    "w4a16_grouped_moe_amd/csrc/dgw4_internal.hpp",

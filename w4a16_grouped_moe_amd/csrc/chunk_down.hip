@@ -34,7 +34,7 @@ long long chunk_grid(const GemmArgs &a, int block_cols)
     return (long long)(a.max_tiles + kXcds - 1) / kXcds * kXcds * ncb;
 }
 
-__global__ void __launch_bounds__(kLwThreads)
+__global__ void __launch_bounds__(wide_threads<kModeDown>())
 __attribute__((amdgpu_waves_per_eu(2))) chunk_down_kernel(GemmArgs p)
 {
     const WideBlock b = wide_block<kModeDown>(p, kChunkDnGroups);
@@ -48,8 +48,8 @@ __attribute__((amdgpu_waves_per_eu(2))) chunk_down_kernel(GemmArgs p)
 hipError_t launch_chunk_down(const GemmArgs &dn, hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;
-    return launch_wide(chunk_down_kernel, wide_lds_bytes<kModeDown, kChunkDnG>(dn.K), allowed,
-                       chunk_grid(dn, kLwCols), dn, stream);
+    return launch_wide<kModeDown>(chunk_down_kernel, wide_lds_bytes<kModeDown, kChunkDnG>(dn.K), allowed,
+                       chunk_grid(dn, wide_cols<kModeDown>()), dn, stream);
 }
 
 }  // namespace dgw4

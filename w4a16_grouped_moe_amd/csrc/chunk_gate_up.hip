@@ -40,7 +40,7 @@ long long chunk_grid(const GemmArgs &a, int block_cols)
     return (long long)(a.max_tiles + kXcds - 1) / kXcds * kXcds * ncb;
 }
 
-__global__ void __launch_bounds__(kLwThreads)
+__global__ void __launch_bounds__(wide_threads<kModeGateUp>())
 __attribute__((amdgpu_waves_per_eu(2))) chunk_gate_up_kernel(GemmArgs p)
 {
     const WideBlock b = wide_block<kModeGateUp>(p, kChunkGuGroups);
@@ -75,8 +75,8 @@ bool chunk_gemms_fit(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g)
 hipError_t launch_chunk_gate_up(const GemmArgs &gu, hipStream_t stream)
 {
     static size_t allowed = 64 * 1024;
-    return launch_wide(chunk_gate_up_kernel, wide_lds_bytes<kModeGateUp, kChunkGuG>(gu.K), allowed,
-                       chunk_grid(gu, kLwCols / 2), gu, stream);
+    return launch_wide<kModeGateUp>(chunk_gate_up_kernel, wide_lds_bytes<kModeGateUp, kChunkGuG>(gu.K), allowed,
+                       chunk_grid(gu, wide_cols<kModeGateUp>() / 2), gu, stream);
 }
 
 }  // namespace dgw4

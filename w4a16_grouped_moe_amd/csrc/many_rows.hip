@@ -30,7 +30,7 @@ hipError_t launch_linear_wide_k(const GemmArgs &a, size_t lds, hipStream_t strea
     const int nblocks = (a.n_out + kLwCols - 1) / kLwCols;
     const int nrb = (a.A + kLwRows - 1) / kLwRows;
     const long long blocks = (long long)(nblocks + kXcds - 1) / kXcds * kXcds * nrb;
-    return launch_wide(linear_wide_kernel<G, NGC, TL, NT>, lds, allowed, blocks, a, stream);
+    return launch_wide<kModeLinear>(linear_wide_kernel<G, NGC, TL, NT>, lds, allowed, blocks, a, stream);
 }
 
 // The many-row dense linear: rows in blocks of 256, each weight dequantised

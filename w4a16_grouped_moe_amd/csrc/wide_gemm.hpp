@@ -58,8 +58,17 @@ enum : int { kModeLinear = 0, kModeGateUp = 1, kModeDown = 2 };
 constexpr int kLwWaves = 8;
 constexpr int kLwThreads = kLwWaves * 64;
 constexpr int kLwRows = 256;                     // rows per block of the dense linear
-constexpr int kLwCols = 256;                     // weight rows per workgroup
+constexpr int kLwCols = 256;                     // weight rows per workgroup of the dense linear
+constexpr int kChunkWaves = 8;                   // waves per workgroup of the chunk GEMMs
 constexpr int kLwNs = 2;                         // 16-row weight tiles per wave
+
+// Waves, threads and weight rows (two 16-row tiles per wave) of a workgroup.
+template <int MODE>
+constexpr int wide_waves() { return MODE == kModeLinear ? kLwWaves : kChunkWaves; }
+template <int MODE>
+constexpr int wide_threads() { return wide_waves<MODE>() * 64; }
+template <int MODE>
+constexpr int wide_cols() { return wide_waves<MODE>() * 16 * kLwNs; }
 constexpr int kLwAhead = 2;                      // weight steps in flight (linear)
 // The chunk modes run few rows per step (an expert's 16 to 128), too little
 // MFMA work to cover a memory latency in one or two steps: gate_up's weights
@@ -69,7 +78,7 @@ constexpr int kLwAhead = 2;                      // weight steps in flight (line
 template <int MODE>
 constexpr int chunk_ahead() { return MODE == kModeGateUp ? 4 : 2; }
 template <int MODE>
-constexpr int chunk_x_ahead() { return MODE == kModeGateUp ? 2 : 1; }
+constexpr int chunk_x_ahead() { return MODE == kModeGateUp && kChunkWaves == 8 ? 2 : 1; }
 constexpr size_t kMaxWideLds = 160 * 1024;       // a CU's LDS: one workgroup per CU
 
 template <int MODE>
@@ -81,7 +90,7 @@ constexpr size_t wide_x_bytes() { return sizeof(uint4) * 2 * wide_rows<MODE>() *
 template <int MODE, int G>
 size_t wide_lds_bytes(int K)
 {
-    return wide_x_bytes<MODE, G>() + 2 * sizeof(uint16_t) * (size_t)kLwCols * (size_t)(K / G);
+    return wide_x_bytes<MODE, G>() + 2 * sizeof(uint16_t) * (size_t)wide_cols<MODE>() * (size_t)(K / G);
 }
 
 // Physical slot of logical 16-byte segment seg of activation row r, an XOR
@@ -151,7 +160,7 @@ __device__ __forceinline__ WideBlock wide_block(const GemmArgs &p, int NG)
         // workgroup -> (chunk, column block): the column blocks of a chunk
         // run on one XCD, back to back, so its activation rows stay in that
         // XCD's L2
-        constexpr int kBlockCols = MODE == kModeGateUp ? kLwCols / 2 : kLwCols;
+        constexpr int kBlockCols = MODE == kModeGateUp ? wide_cols<MODE>() / 2 : wide_cols<MODE>();
         const int ncb = (p.n_out + kBlockCols - 1) / kBlockCols;
         const int chunk = slot / ncb * kXcds + xcd;
         if (chunk >= p.max_tiles)
@@ -184,9 +193,11 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
     constexpr int ROWS = wide_rows<MODE>();
     constexpr int MS = ROWS / 16;                // 16-row MFMA blocks per wave
     constexpr int SEGS = G / 8;                  // 16-byte activation segments per row and step
-    constexpr int XLD = ROWS * SEGS / kLwThreads;   // activation loads per thread and step
+    constexpr int THREADS = wide_threads<MODE>();
+    constexpr int COLS = wide_cols<MODE>();      // weight rows of the workgroup
+    constexpr int XLD = ROWS * SEGS / THREADS;   // activation loads per thread and step
     constexpr int kWords = G / 32;               // k-slices of 32 per group
-    static_assert(ROWS * SEGS % kLwThreads == 0 && kLwThreads % SEGS == 0, "activation split");
+    static_assert(ROWS * SEGS % THREADS == 0 && THREADS % SEGS == 0, "activation split");
     static_assert(MODE == kModeLinear || NGC > 0, "the chunk modes' pipeline needs a static K");
     const int K = p.K;
     const int NG = NGC > 0 ? NGC : K / G;
@@ -211,7 +222,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
     extern __shared__ uint4 lds[];
     uint4 *lds_x = lds;                                           // [2][ROWS][SEGS], swizzled
     uint16_t *lds_s = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(lds) + wide_x_bytes<MODE, G>());
-    uint16_t *lds_z = lds_s + kLwCols * NG;                        // [NG][256] each
+    uint16_t *lds_z = lds_s + COLS * NG;                           // [NG][COLS] each
 
     // ---- scales / zeros of the workgroup's 256 weight rows: [row][group]
     // in memory (512 NG contiguous bytes per array, or two runs of 256 NG for
@@ -221,9 +232,9 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
         const rsrc_t rs = make_rsrc(se, sz_bytes);
         const rsrc_t rz = make_rsrc(ze, sz_bytes);
         constexpr int kRuns = MODE == kModeGateUp ? 2 : 1;
-        constexpr int kRunRows = kLwCols / kRuns;
+        constexpr int kRunRows = COLS / kRuns;
         const int per = kRunRows / 8 * NG;       // 16-byte chunks per run
-        for (int c = tid; c < kRuns * per; c += kLwThreads) {
+        for (int c = tid; c < kRuns * per; c += THREADS) {
             const int run = kRuns == 2 && c >= per ? 1 : 0;
             const int cc = c - run * per;
             const uint32_t base = (uint32_t)(run * p.n_out + col0) * (uint32_t)NG * 2u;
@@ -238,8 +249,8 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
                 // LDS column: gate_up interleaves the runs per 16 rows, so that
                 // wave w's tiles are columns 32 w .. + 15 (gate) and + 16 .. (up)
                 const int col = kRuns == 2 ? (r >> 4) * 32 + run * 16 + (r & 15) : r;
-                lds_s[g * kLwCols + col] = (uint16_t)(sw[j >> 1] >> (16 * (j & 1)));
-                lds_z[g * kLwCols + col] = (uint16_t)(zw[j >> 1] >> (16 * (j & 1)));
+                lds_s[g * COLS + col] = (uint16_t)(sw[j >> 1] >> (16 * (j & 1)));
+                lds_z[g * COLS + col] = (uint16_t)(zw[j >> 1] >> (16 * (j & 1)));
             }
         }
     }
@@ -263,7 +274,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
     // the scalar offset
     const rsrc_t ra = make_rsrc(p.a_src, (uint32_t)p.a_rows * (uint32_t)K * 2u);
     const int xseg = tid % SEGS;
-    constexpr int kRowsPerPass = kLwThreads / SEGS;
+    constexpr int kRowsPerPass = THREADS / SEGS;
     uint32_t xo[MODE == kModeLinear ? 1 : XLD];
     if constexpr (MODE != kModeLinear) {
 #pragma unroll
@@ -371,7 +382,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
             f16x2 cmix[kLwNs], s2[kLwNs];
 #pragma unroll
             for (int ns = 0; ns < kLwNs; ++ns) {
-                const int c = loff + s * kLwCols + lcol + 16 * ns + lrow;   // the lane's weight row
+                const int c = loff + s * COLS + lcol + 16 * ns + lrow;   // the lane's weight row
                 const uint32_t zb = lds_z[c], sb = lds_s[c];
                 cmix[ns] = as_h2(zb | (zb << 16)) + f16x2{(_Float16)1024.0f, (_Float16)64.0f};
                 s2[ns] = as_h2(sb | (sb << 16));
@@ -520,7 +531,7 @@ __device__ __forceinline__ void wide_body(const GemmArgs &p, const WideBlock &b)
     }
 }
 
-template <class Kern>
+template <int MODE, class Kern>
 hipError_t launch_wide(Kern kern, size_t lds, size_t &allowed, long long blocks, const GemmArgs &a,
                        hipStream_t stream)
 {
@@ -531,7 +542,7 @@ hipError_t launch_wide(Kern kern, size_t lds, size_t &allowed, long long blocks,
         return hipErrorInvalidValue;
     if (blocks == 0)
         return hipSuccess;
-    kern<<<dim3((unsigned)blocks), dim3(kLwThreads), lds, stream>>>(a);
+    kern<<<dim3((unsigned)blocks), dim3(wide_threads<MODE>()), lds, stream>>>(a);
     return hipGetLastError();
 }
 
