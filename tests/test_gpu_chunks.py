@@ -182,3 +182,32 @@ def test_chunks_timed_and_graph_replay():
         lc.log(f"[chunks graph] replay {r}")
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {r} differs"
     del g
+
+
+def test_chunks_many_chunks_per_expert_sampled():
+    # 32 experts at T = 2048, top-8: ~512 rows (four chunks) per expert, a
+    # grid of several rounds; 64 sampled tokens against the oracle, the rest
+    # checked for finiteness, and a rerun bitwise equal
+    L = lc.build(lc.custom_shape("chunks_T2048", E=32, topk=8, T=2048, d=2816, m=704, index=99))
+    gu, dn = _tiled(L)
+    s = L.shape
+    assert dg.row_block(s.T, s.topk, s.E, s.d, s.m, gu[3], dn[3]) == 128
+    out = _forward(L, rows="auto")
+    again = _forward(L, rows="auto")
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got.astype(np.float32)))
+    tok = np.random.default_rng(5).choice(s.T, 64, replace=False)
+    tok.sort()
+    lc.assert_close(got[tok], lc.oracle_forward(L, tokens=tok), "chunks T=2048, 64 sampled tokens")
+
+
+def test_chunks_top4_every_token():
+    # E = 64, top-4 at T = 1024: 64 rows per expert, chunks by the library's
+    # choice
+    L = lc.build(lc.custom_shape("chunks_top4", E=64, topk=4, T=1024, d=2816, m=704, index=100))
+    gu, dn = _tiled(L)
+    s = L.shape
+    assert dg.row_block(s.T, s.topk, s.E, s.d, s.m, gu[3], dn[3]) == 128
+    lc.assert_close(_forward(L, rows="auto").cpu().numpy(), lc.oracle_forward(L),
+                    "chunks E=64 top-4 T=1024 (every token)")
