@@ -86,7 +86,7 @@ typedef enum {
  *                     hold many rows. Exists for d = 2816 at gate_up g = 128
  *                     and m = 704 at down g = 64 (else DGW4_ERR_UNSUPPORTED).
  * Neither (the default): chunks when they exist for the shape and the
- * experts hold at least 48 assignments each on average (T * topk >= 48 E),
+ * experts hold at least 22 assignments each on average (T * topk >= 22 E),
  * else tiles. Both bits: DGW4_ERR_INVALID_ARG. The two give the same results
  * up to rounding: tiles apply each group's scale to an fp32 partial, chunks
  * round each dequantised weight (q - z) * s to fp16 once.

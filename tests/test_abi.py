@@ -228,10 +228,10 @@ def test_rows_flags():
         c_data = (A + 128 * 127) * 704 * 2 + A * 2816 * 2
         assert t_data <= tiles < t_data + 256 * 1024
         assert c_data <= chunks < c_data + 256 * 1024
-        # the library's choice: chunks from 48 assignments per expert on
+        # the library's choice: chunks from 22 assignments per expert on
         # average with tiled weights, tiles otherwise
         auto = dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t)
-        assert auto == (chunks if A >= 48 * 128 else tiles)
+        assert auto == (chunks if A >= 22 * 128 else tiles)
         assert dg.workspace_bytes(T, 8, 128, 2816, 704) == tiles
     with pytest.raises(ValueError):
         dg.workspace_bytes(256, 8, 128, 2816, 704, rows="rows")
