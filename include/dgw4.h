@@ -269,8 +269,9 @@ DGW4_API int dgw4_moe_row_block(int T, int topk, int E, int d, int m, int gu_g, 
  * Elapsed time between consecutive events is the duration of one stage.
  * Where alignment, gate_up and down run as one launch (32-row tiles at the
  * layer's shape: d = 2816, m = 704, gate_up g = 128, down g = 64, both
- * stacks in the same layout), events 1, 2 and 3 are all recorded after that launch, so the
- * first stage brackets it and the next two bracket no kernel. events == NULL
+ * stacks in the same layout, E <= 704), events 1, 2 and 3 are all recorded
+ * after that launch, so the first stage brackets it and the next two
+ * bracket no kernel. events == NULL
  * behaves exactly like dgw4_moe_forward; any other n_events is
  * DGW4_ERR_INVALID_ARG. A workspace query (workspace == NULL) records
  * nothing.

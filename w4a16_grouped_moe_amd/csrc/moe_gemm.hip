@@ -803,8 +803,19 @@ __device__ inline void load_ids(const int32_t *__restrict__ ids, int A, int c0, 
 
 // The tile's expert, or -1 when the tile lies past the padded total. Ids
 // outside [0, E) are skipped. Also sets every s_rows entry to A (pad).
-__device__ int layer_tile_find(const int32_t *__restrict__ ids, int A, int E, int tile, TileSetup &ts,
-                               int *s_cnt, int *s_wsum, int *s_rows, int *s_info)
+// The tile of the workgroup in slot tslot of XCD xcd: with n tiles in all,
+// XCD x takes tiles x ceil(n / 8) .. + ceil(n / 8) - 1, so that the tiles of
+// an expert with several (in expert order, consecutive) run on one XCD at
+// the same time and read its weights through one L2; -1 past the last.
+__device__ inline int layer_tile_of(int xcd, int tslot, int total_rows)
+{
+    const int ntiles = total_rows / kBlockM;
+    const int per = (ntiles + kXcds - 1) / kXcds;
+    return tslot < per ? xcd * per + tslot : -1;
+}
+
+__device__ int layer_tile_find(const int32_t *__restrict__ ids, int A, int E, int xcd, int tslot,
+                               TileSetup &ts, int *s_cnt, int *s_wsum, int *s_rows, int *s_info)
 {
     const int tid = threadIdx.x;
     for (int x = tid; x < E; x += kL4Threads)
@@ -828,22 +839,21 @@ __device__ int layer_tile_find(const int32_t *__restrict__ ids, int A, int E, in
                 atomicAdd(&s_cnt[v[j]], 1);
     }
     __syncthreads();
-    // padded offsets in expert order; the expert whose rows hold the tile's first
-    const int row = tile * kBlockM;
-    int base = 0;
-    for (int e0 = 0; e0 < E; e0 += kL4Threads) {
-        const int e = e0 + tid;
-        const int cnt = e < E ? s_cnt[e] : 0;
-        const int padded = (cnt + kBlockM - 1) / kBlockM * kBlockM;
-        int total;
-        const int off = base + l4_scan_excl(padded, s_wsum, total);
-        if (e < E && off <= row && row < off + padded) {
-            s_info[0] = e;
-            s_info[1] = off;
-            s_info[2] = cnt;
-            s_info[3] = padded / kBlockM;
-        }
-        base += total;
+    // padded offsets in expert order, one expert per thread (E <=
+    // kL4Threads, see layer_fused); the tile follows from the total (see
+    // layer_tile_of), and the thread whose expert's rows hold the tile's
+    // first row records it
+    const int cnt = tid < E ? s_cnt[tid] : 0;
+    const int padded = (cnt + kBlockM - 1) / kBlockM * kBlockM;
+    int total;
+    const int off = l4_scan_excl(padded, s_wsum, total);
+    const int tile = layer_tile_of(xcd, tslot, total);
+    const int row = tile < 0 ? INT_MAX : tile * kBlockM;
+    if (tid < E && off <= row && row < off + padded) {
+        s_info[0] = tid;
+        s_info[1] = off;
+        s_info[2] = cnt;
+        s_info[3] = padded / kBlockM;
     }
     __syncthreads();
     // uniform over the workgroup: scalar registers
@@ -1337,9 +1347,12 @@ __device__ __forceinline__ void layer_body(const GemmArgs &gu, const GemmArgs &d
     down_ks_body<NMS, TL, NT>(dn, e, h, s_rows, valid, pf, s_next);
 }
 
-// Workgroup -> (half, tile), both halves of a tile on one XCD (consecutive
-// workgroups go to the 8 XCDs in turn), so a tile's activation rows stay in
-// one L2. Y gets the two fp16 partials [2][A][d] at each assignment's flat id.
+// Workgroup -> (half, tile): consecutive workgroups go to the 8 XCDs in
+// turn, and slot s of XCD x takes half s % 2 of tile layer_tile_of(x, s / 2),
+// a contiguous block of tiles per XCD: both halves of a tile share one L2
+// (its activation rows), and so do the tiles of an expert with several (its
+// weights). Y gets the two fp16 partials [2][A][d] at each assignment's flat
+// id.
 template <bool TL>
 __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs dn,
                                                            const int32_t *__restrict__ ids, int E)
@@ -1351,11 +1364,8 @@ __global__ void __launch_bounds__(kL4Threads) layer_kernel(GemmArgs gu, GemmArgs
     __shared__ int s_next;
     const int xcd = (int)blockIdx.x % kXcds, slot = (int)blockIdx.x / kXcds;
     const int h = slot % 2;
-    const int tile = slot / 2 * kXcds + xcd;
-    if (tile >= gu.max_tiles)
-        return;
     TileSetup ts;
-    const int e = layer_tile_find(ids, gu.A, E, tile, ts, s_cnt, s_wsum, s_rows, s_info);
+    const int e = layer_tile_find(ids, gu.A, E, xcd, slot / 2, ts, s_cnt, s_wsum, s_rows, s_info);
     if (e < 0)
         return;
     auto rows = [&]() { layer_tile_rows(ids, gu.A, e, ts, s_wsum, s_rows); };
@@ -1730,9 +1740,9 @@ hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
 bool layer_fused(const GemmArgs &gu, int gu_g, const GemmArgs &dn, int dn_g, int E)
 {
     // (the layer kernel stores each Y partial through 32-bit byte offsets
-    // below 2^31)
+    // below 2^31, and its alignment takes one expert per thread)
     return layer_shape_gate_up(gu, gu_g) && dn_g == 64 && layer_shape_down(dn, dn_g) &&
-           gu.tiled == dn.tiled && E <= kMaxExperts && (long long)dn.A * dn.n_out * 2 < (1LL << 31);
+           gu.tiled == dn.tiled && E <= kL4Threads && (long long)dn.A * dn.n_out * 2 < (1LL << 31);
 }
 
 hipError_t launch_layer(const GemmArgs &gu, const GemmArgs &dn, const int32_t *ids, int E,
