@@ -121,7 +121,6 @@ __device__ inline f16x8 dequant8(uint32_t w, f16x2 c1024, f16x2 c64)
     return r;
 }
 
-// fp16(1024 + z) and fp16(64 + z) as packed pairs; exact for -2033 <= z <= 1024
 // The same eight nibbles as fp16 weights (q - z) * s in natural K order
 // (n0 .. n7). A byte permute puts byte b at bytes 0 and 2, so that one mask
 // takes its low nibble to bits 0-3 (fp16 1024 + n) and its high nibble to
@@ -141,6 +140,7 @@ __device__ inline f16x8 dequant8_scaled(uint32_t w, f16x2 cmix, f16x2 s2)
     return r;
 }
 
+// fp16(1024 + z) and fp16(64 + z) as packed pairs; exact for -2033 <= z <= 1024
 __device__ inline void zero_point_consts(uint32_t zbits, f16x2 &c1024, f16x2 &c64)
 {
     const f16x2 zz = as_h2(zbits | (zbits << 16));
