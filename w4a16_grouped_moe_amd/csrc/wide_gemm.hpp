@@ -29,9 +29,10 @@ namespace {
 // group per step: each wave loads its tiles' share of the group (16 or 8
 // bytes per lane and tile) P steps ahead, and the workgroup stages the
 // step's activation slice (the block's rows x G values, as loaded) in a
-// double-buffered LDS area from registers loaded one step ahead, one barrier
-// per step; the slots of a row are XOR-swizzled so that the 16 rows one MFMA
-// fragment reads hit distinct banks. The weights are the MFMA's row operand,
+// double-buffered LDS area from registers loaded ahead of it (the linear: in
+// two halves, each half a step ahead; the chunk modes: whole, one or two
+// steps ahead), one barrier per step; the slots of a row are XOR-swizzled so
+// that the 16 rows one MFMA fragment reads hit distinct banks. The weights are the MFMA's row operand,
 // so a lane holds one weight row per tile: it forms that row's fp16 weights
 // (q - z) * s for the group (q - z exact, one rounding of the product), in
 // natural K order, and the MFMA accumulates all groups in fp32; a lane ends
