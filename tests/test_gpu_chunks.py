@@ -9,7 +9,8 @@ boundary, empty experts, experts with three chunks and a ragged last one
 (Zipf routing at T = 300 over 16 experts), duplicate and dropped ids, the
 routed entry point, the full-size workloads (T = 256 uniform and skewed on
 chunks; T = 1024, which takes chunks by default, also on 32-row tiles),
-determinism over reruns with stale workspace contents, and graph replay.
+determinism over reruns with stale workspace contents, graph replay, and
+1024 experts of which 7 hold rows (on chunks and on tiles).
 """
 import numpy as np
 import pytest
@@ -211,3 +212,39 @@ def test_chunks_top4_every_token():
     assert dg.row_block(s.T, s.topk, s.E, s.d, s.m, gu[3], dn[3]) == 128
     lc.assert_close(_forward(L, rows="auto").cpu().numpy(), lc.oracle_forward(L),
                     "chunks E=64 top-4 T=1024 (every token)")
+
+
+def _scatter_experts(pack, slots, E):
+    # a device pack of E experts whose experts slots[i] hold pack's expert i
+    # (the rest zero, never routed to)
+    q, s, z, g = pack
+    out = []
+    for a in (q, s, z):
+        big = torch.zeros((E,) + tuple(a.shape[1:]), dtype=a.dtype, device=a.device)
+        big[torch.as_tensor(slots, device=a.device)] = a
+        out.append(big)
+    return (*out, g)
+
+
+@pytest.mark.parametrize("rows", ["chunks", "tiles"])
+def test_many_experts_few_live(rows):
+    # E = 1024 (the largest expert count) with 7 live experts spread over it
+    # (0 .. 1023), the others empty: the alignment's per-expert workgroups and
+    # offsets over 1024 experts; on tiles the layer kernel does not take so
+    # many experts, so the separate alignment and GEMMs run
+    E = 1024
+    slots = [0, 63, 64, 130, 511, 700, 1023]
+    T, topk = 200, 4
+    rng = np.random.default_rng(13)
+    small = np.stack([rng.choice(len(slots), topk, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0.1, 1, (T, topk)).astype(np.float32)
+    L = lc.build(lc.custom_shape(f"many_experts_{rows}", E=len(slots), topk=topk, T=T, d=2816, m=704,
+                                 index=101), ids=small, w=w)
+    ref = lc.oracle_forward(L)
+    gu, dn = _tiled(L)
+    gu_big, dn_big = _scatter_experts(gu, slots, E), _scatter_experts(dn, slots, E)
+    big_ids = torch.as_tensor(np.asarray(slots, np.int32)[small], device="cuda")
+    lc.log(f"[many experts] live expert rows {np.bincount(small.ravel()).tolist()}")
+    o = dg.moe_forward(L.x_dev, big_ids, L.w_dev, gu_big, dn_big, rows=rows)
+    torch.cuda.synchronize()
+    lc.assert_close(o.cpu().numpy(), ref, f"E={E} on {rows}, 7 live experts")
