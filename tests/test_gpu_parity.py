@@ -203,6 +203,24 @@ def test_forward_full_deterministic_100(full_layer):
     assert bad == 0
 
 
+@pytest.mark.parametrize("rows", ["tiles", "chunks"])
+def test_forward_out_8_byte_aligned(full_layer, rows):
+    # an output at the API's minimum alignment (8 bytes, not 16) gets the same
+    # bits as a fresh tensor and nothing outside it is written, on the two Y
+    # layouts (two partials on tiles, one array on chunks)
+    L = full_layer
+    T, d = L.shape.T, L.shape.d
+    gu, dn = (dg.pack_tiled(L.gu_dev), dg.pack_tiled(L.dn_dev)) if rows == "chunks" else (L.gu_dev, L.dn_dev)
+    ref = dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, rows=rows)
+    buf = torch.full((T * d + 4,), float("nan"), dtype=torch.float16, device="cuda")
+    out = buf[4:].view(T, d)
+    assert out.data_ptr() % 16 == 8
+    dg.moe_forward(L.x_dev, L.ids_dev, L.w_dev, gu, dn, out=out, rows=rows)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert torch.isnan(buf[:4]).all()
+
+
 def test_forward_layer_shape_unfused_every_token():
     # gate_up with g=64 at the layer's shape: the generic gate_up kernel, then
     # the layer-shape down kernel as a launch of its own
