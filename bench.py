@@ -218,6 +218,58 @@ def mfma_probe(torch, dg, dev, iters: int = 20000, reps: int = 5) -> dict:
             "tflops": round(tflops, 1)}
 
 
+def _time_calls(torch, fn, calls: int) -> float:
+    """us per call of fn over `calls` back-to-back calls (after two warm-ups)."""
+    fn()
+    fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(calls):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / calls
+
+
+def dense_comparison(torch, dg, dev, xd, w4, w4_us: float, calls: int) -> dict:
+    """The pages compare their dense W4A16 kernels with the dense 16-bit GEMM
+    at 256 rows (an LM-head tile, QKV). Here: torch's F.linear (hipBLASLt) in
+    bf16 and fp16 on the same x and a random [N, K] weight of the same size,
+    at the LM-head shape, and at 256 x 2816 x N for N = 4096 .. 16384 against
+    this library's linear (the pages give no QKV width, so a range of widths
+    stands in for one)."""
+    import torch.nn.functional as F
+    T, K = xd.shape
+    N = 262144
+    out = {"lmhead": {"w4a16_us": round(w4_us, 1)}}
+    for name, dt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        wd = torch.randn((N, K), device=dev, dtype=dt)
+        xt = xd.to(dt)
+        us = _time_calls(torch, lambda: F.linear(xt, wd), calls)
+        out["lmhead"][f"{name}_us"] = round(us, 1)
+        out["lmhead"][f"w4a16_speedup_vs_{name}"] = round(us / w4_us, 3)
+        del wd, xt
+    log(f"[linear] F.linear at the LM-head shape: bf16 {out['lmhead']['bf16_us']} us, "
+        f"f16 {out['lmhead']['f16_us']} us; W4A16 {w4_us:.1f} us")
+    rows = []
+    if w4 is not None:
+        for n in (4096, 8192, 16384):
+            wq = tuple(t[:n] for t in w4[:3]) + (w4[3],)      # the first n rows of the tiled matrix
+            w4us = _time_calls(torch, lambda: dg.w4a16_linear(xd, wq), 50)
+            wd = torch.randn((n, K), device=dev, dtype=torch.bfloat16)
+            xt = xd.to(torch.bfloat16)
+            bus = _time_calls(torch, lambda: F.linear(xt, wd), 50)
+            rows.append({"N": n, "w4a16_us": round(w4us, 1), "bf16_us": round(bus, 1),
+                         "w4a16_speedup_vs_bf16": round(bus / w4us, 3),
+                         "row_block": dg.linear_row_block(T, K, n, w4[3])})
+            log(f"[linear] T={T} K={K} N={n}: W4A16 {w4us:.1f} us, bf16 F.linear {bus:.1f} us")
+            del wd, xt
+        out["narrow"] = rows
+    return out
+
+
 def bench_linear(torch, dg, dev, args) -> int:
     """The dense W4A16 linear at an LM-head shape: x fp16 [256, 2816] against
     one packed [262144, 2816] matrix (392 MB of nibbles, scales and zeros:
@@ -256,6 +308,9 @@ def bench_linear(torch, dg, dev, args) -> int:
     flops = 2 * T * K * N
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"[linear] {steps} calls: {ms * 1e3:.1f} us each, {gbps:.1f} GB/s, {tflops:.1f} TFLOP/s")
+    del y
+    dense = dense_comparison(torch, dg, dev, xd, w if args.weight_layout == "tiled" else None,
+                             ms * 1e3, steps)
     probe = mfma_probe(torch, dg, dev)
     probe["pct_of_probe"] = round(100 * tflops / probe["tflops"], 2)
     log(f"[linear] MFMA probe {probe['tflops']} TFLOP/s; the linear at {probe['pct_of_probe']}% of it")
@@ -270,6 +325,7 @@ def bench_linear(torch, dg, dev, args) -> int:
         "us_per_call": round(ms * 1e3, 2), "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_call": nbytes,
         "mfma_probe": probe,
+        "dense_f16_bf16": dense,
         # 2 T K N FLOP over 392 MB of weights is 4 T = 1024 FLOP per byte,
         # far past the fp16 ridge (2.5 PFLOP/s over 8 TB/s = 312): MFMA-bound
         "roofline": {"kernel": (f"linear_wide_kernel<128, 22, {str(args.weight_layout == 'tiled').lower()}, "

@@ -323,18 +323,37 @@ DGW4_API int dgw4_moe_experts(const uint16_t *x, const int32_t *topk_ids, int T,
  *   q  uint8 [N, K/2], s and z fp16 [N, K/g]: one matrix in the layout of
  *      dgw4_quantize_rtn with E = 1 (16-byte aligned);
  *   y  fp16 [T, N] row-major (written, caller-owned).
- * Each output is the fp32 sum over K of x times (q - z) with the group's
- * scale applied once per group in fp32, rounded once to fp16.
- * g may carry DGW4_WEIGHTS_TILED (q in the tiled layout; same results).
- * Returns DGW4_ERR_INVALID_ARG for null pointers (T > 0), negative T, odd K,
- * K % g != 0, unknown flag bits in g or misaligned pointers;
- * DGW4_ERR_UNSUPPORTED for g not in {64, 128}, N not a multiple of 16, more
- * than 64 groups per row, or tensors past 2 GiB. T == 0 is a no-op. Enqueued
- * on `stream`, no host sync.
+ * g may carry DGW4_WEIGHTS_TILED (q in the tiled layout; same results) and
+ * one of the row-block flags, which pick the kernel:
+ *   DGW4_ROWS_TILES   32-row tiles: each output is the fp32 sum over K of x
+ *                     times the exact integers (q - z), the group's scale
+ *                     applied once per group in fp32;
+ *   DGW4_ROWS_CHUNKS  the many-row kernel (256-row blocks): each weight is
+ *                     formed once per block as fp16 (q - z) * s (one
+ *                     rounding) and the MFMA sums over K in fp32; needs y
+ *                     8-byte aligned and K small enough for its LDS staging
+ *                     (else DGW4_ERR_UNSUPPORTED);
+ *   neither           the many-row kernel where it fits, T >= 128 and
+ *                     T * N >= 2^23 (enough 256 x 256 blocks to cover half
+ *                     the chip), else the tiles.
+ * Either way the result is rounded once to fp16; the two agree up to that
+ * rounding of the weights. Returns DGW4_ERR_INVALID_ARG for null pointers
+ * (T > 0), negative T, odd K, K % g != 0, unknown flag bits or both row
+ * flags in g, or misaligned pointers; DGW4_ERR_UNSUPPORTED for g not in
+ * {64, 128}, N not a multiple of 16, more than 64 groups per row, or
+ * tensors past 2 GiB. T == 0 is a no-op. Enqueued on `stream`, no host sync.
  */
 DGW4_API int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
                                const uint16_t *s, const uint16_t *z, int g, uint16_t *y,
                                void *stream);
+
+/*
+ * dgw4_linear_row_block — the row block of the kernel dgw4_w4a16_linear
+ * runs for these sizes and g (flags included) with an 8-byte aligned y: 32
+ * (the 32-row tiles) or 256 (the many-row kernel); a negative status code
+ * (-DGW4_ERR_...) where the call would fail its checks. Launches nothing.
+ */
+DGW4_API int dgw4_linear_row_block(int T, int K, int N, int g);
 
 /*
  * dgw4_sample — the sampler of a denoising step, in one streaming pass over

@@ -197,7 +197,8 @@ def test_layout_flag_bits():
     assert n == dg.workspace_bytes(256, 8, 128, 2816, 704)
     f = dg.lib().dgw4_w4a16_linear
     p = 1 << 12
-    assert f(p, 4, 256, 64, p, p, p, 64 | 0x40000, p, None) == B.ERR_INVALID_ARG
+    assert f(p, 4, 256, 64, p, p, p, 64 | 0x80000, p, None) == B.ERR_INVALID_ARG
+    assert f(p, 4, 256, 64, p, p, p, 64 | B.ROWS_TILES | B.ROWS_CHUNKS, p, None) == B.ERR_INVALID_ARG
     assert f(None, 0, 256, 64, None, None, None, 64 | tiled, None, None) == B.OK
 
 
@@ -243,6 +244,29 @@ def test_rows_flags():
     assert dg.row_block(1024, 8, 128, 2816, 704, 128 | t, 64 | t, rows="tiles") == 32
     assert dg.lib().dgw4_moe_row_block(4, 2, 8, 512, 192, 128 | B.ROWS_CHUNKS, 64) == -B.ERR_UNSUPPORTED
     assert dg.lib().dgw4_moe_row_block(4, 9, 8, 512, 192, 128, 64) == -B.ERR_INVALID_ARG
+
+
+def test_linear_row_block():
+    # the dense linear's kernel: many-row (256) from 128 rows on once
+    # T * N >= 2^23, else 32-row tiles; forced either way by the row flags
+    t = dg.WEIGHTS_TILED
+    for T, N, want in [(256, 16384, 32), (512, 16384, 256), (128, 32768, 32), (128, 65536, 256),
+                       (1024, 8192, 256), (1024, 4096, 32), (127, 1 << 20, 32), (256, 262144, 256),
+                       (0, 262144, 32)]:
+        assert dg.linear_row_block(T, 2816, N, 128 | t) == want, (T, N)
+        assert dg.linear_row_block(T, 2816, N, 128) == want, (T, N)
+    assert dg.linear_row_block(256, 2816, 16384, rows="chunks") == 256
+    assert dg.linear_row_block(1, 512, 48, rows="chunks") == 256
+    assert dg.linear_row_block(256, 2816, 262144, rows="tiles") == 32
+    f = dg.lib().dgw4_linear_row_block
+    assert f(256, 2816, 16384, 128 | B.ROWS_TILES | B.ROWS_CHUNKS) == -B.ERR_INVALID_ARG
+    assert f(256, 2816, 16384, 96) == -B.ERR_UNSUPPORTED
+    assert f(256, 2816, 16390, 128) == -B.ERR_UNSUPPORTED
+    assert f(-1, 2816, 16384, 128) == -B.ERR_INVALID_ARG
+    # K too large for the many-row kernel's LDS staging: tiles by choice,
+    # refused when asked for
+    assert f(256, 64 * 128, 1 << 16, 128) == 32
+    assert f(256, 64 * 128, 1 << 16, 128 | B.ROWS_CHUNKS) == -B.ERR_UNSUPPORTED
 
 
 def test_sample_noalloc_rejects():

@@ -131,14 +131,15 @@ def test_forward_tiled_unfused_layer_shape():
     lc.assert_close(_forward_pair(L), lc.oracle_forward(L), "tiled unfused (all 64 tokens)")
 
 
+@pytest.mark.parametrize("rows", ["tiles", "chunks"])
 @pytest.mark.parametrize("g,T,K,N", [(128, 37, 2816, 1408), (64, 70, 704, 2816), (128, 1, 512, 48),
                                      (128, 300, 2816, 1408), (64, 256, 1024, 384)])
-def test_linear_tiled_equals_canonical(g, T, K, N):
+def test_linear_tiled_equals_canonical(g, T, K, N, rows):
     x, wf = linear_inputs(11, T, K, N)
     q, s, z = dg.quantize_rtn(torch.from_numpy(wf).cuda(), g)
     xd = torch.from_numpy(x).cuda()
-    canon = dg.w4a16_linear(xd, (q, s, z, g)).clone()
-    tiled = dg.w4a16_linear(xd, _tiled((q, s, z, g)))
+    canon = dg.w4a16_linear(xd, (q, s, z, g), rows=rows).clone()
+    tiled = dg.w4a16_linear(xd, _tiled((q, s, z, g)), rows=rows)
     torch.cuda.synchronize()
     assert torch.equal(tiled.view(torch.int16), canon.view(torch.int16))
 

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     version,
     workspace_bytes,
     row_block,
+    linear_row_block,
     w4a16_linear,
     sample,
     sample_noalloc,

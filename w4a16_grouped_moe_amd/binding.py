@@ -67,6 +67,8 @@ def lib():
                                              ctypes.POINTER(P), I]
         L.dgw4_w4a16_linear.restype = I
         L.dgw4_w4a16_linear.argtypes = [P, I, I, I, P, P, P, I, P, P]
+        L.dgw4_linear_row_block.restype = I
+        L.dgw4_linear_row_block.argtypes = [I, I, I, I]
         L.dgw4_moe_experts.restype = I
         L.dgw4_moe_experts.argtypes = [P, P, I, I, I, I, I, P, P, P, I, P, P, P, I,
                                        P, ctypes.POINTER(S), P]
@@ -183,12 +185,16 @@ def pack_tiled(w: tuple) -> tuple:
     return qt, s, z, g | WEIGHTS_TILED
 
 
-def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> torch.Tensor:
+def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None,
+                 rows: str = "auto") -> torch.Tensor:
     """Dense W4A16 linear: y = x * deq(W)^T.
 
     x fp16 [T, K]; w = (q uint8 [N, K/2], s fp16 [N, K/g], z fp16 [N, K/g], g),
-    e.g. one matrix of quantize_rtn, or its pack_tiled form. Returns y fp16 [T, N]."""
+    e.g. one matrix of quantize_rtn, or its pack_tiled form. Returns y fp16 [T, N].
+    ``rows``: "auto", "tiles" (32-row tiles) or "chunks" (the many-row
+    kernel, 256-row blocks), see dgw4_w4a16_linear in include/dgw4.h."""
     q, s, z, g = w
+    g |= _rows_flag(rows)
     T, K = x.shape
     N = q.shape[0]
     if q.shape != (N, K // 2) or s.shape != (N, K // _group(g)) or z.shape != s.shape:
@@ -204,6 +210,15 @@ def w4a16_linear(x: torch.Tensor, w: tuple, out: torch.Tensor | None = None) -> 
     py = _dev(out, "out", _F16)
     _check("dgw4_w4a16_linear", lib().dgw4_w4a16_linear(px, T, K, N, pq, ps, pz, g, py, _stream(x)))
     return out
+
+
+def linear_row_block(T: int, K: int, N: int, g: int = 128, rows: str = "auto") -> int:
+    """The row block of the kernel w4a16_linear runs for these sizes and g
+    (with its layout bit): 32 (tiles) or 256 (the many-row kernel)."""
+    r = lib().dgw4_linear_row_block(T, K, N, g | _rows_flag(rows))
+    if r < 0:
+        _check("dgw4_linear_row_block", -r)
+    return r
 
 
 def sample(logits: torch.Tensor, seed: int = 0, entropy: bool = True, draw: bool = True,

@@ -469,11 +469,15 @@ int dgw4_mfma_probe(int iters, uint32_t *sink, double *flops, void *stream)
     return from_hip(dgw4::launch_mfma_probe(iters, sink, flops, (hipStream_t)stream));
 }
 
-int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
-                      const uint16_t *s, const uint16_t *z, int garg, uint16_t *y, void *stream)
+namespace {
+
+// The dense linear's checks and arguments; query (y unused) leaves the
+// kernel's row block in *row_block instead of launching it.
+int linear_impl(const uint16_t *x, int T, int K, int N, const uint8_t *q, const uint16_t *s,
+                const uint16_t *z, int garg, uint16_t *y, void *stream, int *row_block)
 {
-    int g = 0, tiled = 0;
-    if (!split_group(garg, g, tiled))
+    int g = 0, tiled = 0, rows = 0;
+    if (!split_rows(garg, rows) || !split_group(garg, g, tiled))
         return DGW4_ERR_INVALID_ARG;
     if (T < 0 || K < 2 || (K % 2) != 0 || N < 1 || g < 1)
         return DGW4_ERR_INVALID_ARG;
@@ -488,11 +492,12 @@ int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
         (long long)T * K * 2 >= (1LL << 31) || (long long)T * N * 2 >= (1LL << 31) ||
         (long long)N * K / 2 >= (1LL << 31))
         return DGW4_ERR_UNSUPPORTED;
-    if (T == 0)
+    if (T == 0 && !row_block)
         return DGW4_OK;
-    if (!x || !q || !s || !z || !y)
+    if (!row_block && (!x || !q || !s || !z || !y))
         return DGW4_ERR_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 16) || !aligned(z, 16) || !aligned(y, 2))
+    if (!row_block &&
+        (!aligned(x, 16) || !aligned(q, 16) || !aligned(s, 16) || !aligned(z, 16) || !aligned(y, 2)))
         return DGW4_ERR_INVALID_ARG;
     dgw4::GemmArgs a{};
     a.a_src = x;
@@ -508,7 +513,29 @@ int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
     a.max_tiles = (T + dgw4::kBlockM - 1) / dgw4::kBlockM;
     a.out = y;
     a.tiled = tiled;
-    return from_hip(dgw4::launch_linear(a, g, (hipStream_t)stream));
+    const int rb = dgw4::linear_row_block(a, g, rows);
+    if (rb < 0)
+        return DGW4_ERR_UNSUPPORTED;
+    if (row_block) {
+        *row_block = rb;
+        return DGW4_OK;
+    }
+    return from_hip(dgw4::launch_linear(a, g, rb, (hipStream_t)stream));
+}
+
+}  // namespace
+
+int dgw4_w4a16_linear(const uint16_t *x, int T, int K, int N, const uint8_t *q,
+                      const uint16_t *s, const uint16_t *z, int garg, uint16_t *y, void *stream)
+{
+    return linear_impl(x, T, K, N, q, s, z, garg, y, stream, nullptr);
+}
+
+int dgw4_linear_row_block(int T, int K, int N, int g)
+{
+    int rb = 0;
+    const int st = linear_impl(nullptr, T, K, N, nullptr, nullptr, nullptr, g, nullptr, nullptr, &rb);
+    return st == DGW4_OK ? rb : -st;
 }
 
 int dgw4_pack_tiled(const uint8_t *q, int E, int N, int K, int g, uint8_t *qt, void *stream)

@@ -80,8 +80,14 @@ hipError_t launch_gate_up(const GemmArgs &a, int g, hipStream_t stream);
 
 // Dense linear y = x * deq(W)^T over the a.A = a_rows rows of x in order:
 // a.sorted_ids / a.tile_info unused, one weight matrix (n_w = n_out = N rows),
-// a.out = y fp16 [A, N] in natural column order.
-hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream);
+// a.out = y fp16 [A, N] in natural column order. linear_row_block gives the
+// kernel for the caller's choice rows (0, DGW4_ROWS_TILES or
+// DGW4_ROWS_CHUNKS): kBlockM (32-row tiles), kLinearWideRows (the many-row
+// kernel) or -1 (the many-row kernel asked for where it does not fit);
+// launch_linear runs the one given.
+constexpr int kLinearWideRows = 256;
+int linear_row_block(const GemmArgs &a, int g, int rows);
+hipError_t launch_linear(const GemmArgs &a, int g, int row_block, hipStream_t stream);
 
 // The many-row dense linear (many_rows.hip): whether its LDS and alignment needs
 // hold for a, and its launch (a.A rows in 256-row blocks).

@@ -70,6 +70,7 @@
 // host readback); the workgroups of one tile run on one XCD so that its
 // activation rows stay in that XCD's L2; tiles with at most 16 valid rows run
 // one 16-row MFMA block instead of two.
+#include "dgw4.h"
 #include "dgw4_internal.hpp"
 #include "gemm_common.hpp"
 
@@ -1725,12 +1726,33 @@ hipError_t launch_down(const GemmArgs &a, int g, hipStream_t stream)
     return g == 128 ? launch_down_g<128, false>(a, stream) : launch_down_g<64, false>(a, stream);
 }
 
-// Rows from which the dense linear takes the many-row kernel.
+// With no choice given, the dense linear takes the many-row kernel from 128
+// rows on once T * N >= 2^23, i.e. its 256-row x 256-column workgroups
+// would cover 128 CUs at full row blocks. Below that the many-row grid is
+// too small to fill the chip: each workgroup runs the whole K (about 65 us
+// at K = 2816), so one round of a few workgroups costs as much as a full
+// one, while the 32-row tiles spread the same work over many workgroups.
+// Measured at K = 2816, g = 128 (us, tiles against many-row): T = 256,
+// N = 16384: 47.5 / 68.9; T = 512, N = 16384: 91.3 / 73.0; T = 128,
+// N = 32768: 47.7 / 66.9; T = 128, N = 65536: 90.3 / 72.6; the rule picks
+// the faster kernel at all 28 points of N = 2^11 .. 2^17 x T = 128 .. 1024.
 constexpr int kLinearWideMinRows = 128;
+constexpr long long kLinearWideMinWork = 1LL << 23;   // T * N
 
-hipError_t launch_linear(const GemmArgs &a, int g, hipStream_t stream)
+int linear_row_block(const GemmArgs &a, int g, int rows)
 {
-    if (a.A >= kLinearWideMinRows && linear_wide_fits(a, g))
+    const bool fits = linear_wide_fits(a, g);
+    if (rows == DGW4_ROWS_CHUNKS)
+        return fits ? kLinearWideRows : -1;
+    if (rows == DGW4_ROWS_TILES)
+        return kBlockM;
+    const bool wide = fits && a.A >= kLinearWideMinRows && (long long)a.A * a.n_out >= kLinearWideMinWork;
+    return wide ? kLinearWideRows : kBlockM;
+}
+
+hipError_t launch_linear(const GemmArgs &a, int g, int row_block, hipStream_t stream)
+{
+    if (row_block == kLinearWideRows)
         return launch_linear_wide(a, g, stream);
     if (a.tiled)
         return g == 128 ? launch_linear_g<128, true>(a, stream) : launch_linear_g<64, true>(a, stream);
