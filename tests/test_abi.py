@@ -246,6 +246,23 @@ def test_rows_flags():
     assert dg.lib().dgw4_moe_row_block(4, 9, 8, 512, 192, 128, 64) == -B.ERR_INVALID_ARG
 
 
+def test_largest_token_counts():
+    # the layer's 32-bit offsets bound T: on tiles H (T * 8 + 31 E padded rows
+    # x m x 2 bytes) stays under 2 GiB up to T = 190154 at E = 128; on chunks
+    # Y (T * 8 x d x 2 bytes) up to T = 47662; one more token is refused
+    t = dg.WEIGHTS_TILED
+    for T, rows, ok in [(190154, "tiles", True), (190155, "tiles", False),
+                        (47662, "chunks", True), (47663, "chunks", False)]:
+        if ok:
+            assert dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t, rows=rows) > 0
+        else:
+            with pytest.raises(dg.Dgw4Error, match="UNSUPPORTED"):
+                dg.workspace_bytes(T, 8, 128, 2816, 704, 128 | t, 64 | t, rows=rows)
+    # past the chunks' limit the library's choice is the tiles
+    assert dg.row_block(47663, 8, 128, 2816, 704, 128 | t, 64 | t) == 32
+    assert dg.row_block(47662, 8, 128, 2816, 704, 128 | t, 64 | t) == 128
+
+
 def test_linear_row_block():
     # the dense linear's kernel: many-row (256) from 128 rows on once
     # T * N >= 2^23, else 32-row tiles; forced either way by the row flags
