@@ -73,7 +73,8 @@ int from_hip(hipError_t e)
 // arrays, the partials of the two halves of down's contraction; on 128-row
 // chunks the alignment, H and one Y are used.
 struct Layout {
-    size_t counts, offsets, num_padded, tile_expert, tile_info, sorted_ids, h, y, rids, rw, total;
+    size_t counts, offsets, num_padded, tile_expert, tile_info, tile_order, sorted_ids, h, y, rids, rw,
+        total;
 };
 
 Layout layout(long long A, int T, int E, int d, int m, long long cap, int block_m, int halves)
@@ -90,6 +91,7 @@ Layout layout(long long A, int T, int E, int d, int m, long long cap, int block_
     L.num_padded = take(sizeof(int32_t));
     L.tile_expert = take(sizeof(int32_t) * (size_t)(cap / block_m));
     L.tile_info = take(sizeof(int2) * (size_t)(cap / block_m));
+    L.tile_order = take(sizeof(int32_t) * (size_t)(cap / block_m));
     L.sorted_ids = take(sizeof(int32_t) * (size_t)cap);
     L.h = take(sizeof(uint16_t) * (size_t)cap * (size_t)m);
     L.y = take((size_t)halves * sizeof(uint16_t) * (size_t)A * (size_t)d);
@@ -160,7 +162,7 @@ int dgw4_align(const int32_t *topk_ids, int T, int topk, int E, int block_m, int
         return DGW4_ERR_INVALID_ARG;
     return from_hip(dgw4::launch_align(topk_ids, T * topk, E, block_m, (long long)cap, counts,
                                        offsets, sorted_ids, tile_expert, num_padded, nullptr,
-                                       (hipStream_t)stream));
+                                       nullptr, (hipStream_t)stream));
 }
 
 namespace {
@@ -287,12 +289,15 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     int32_t *num_padded = reinterpret_cast<int32_t *>(ws + L.num_padded);
     int32_t *tile_expert = reinterpret_cast<int32_t *>(ws + L.tile_expert);
     int2 *tile_info = reinterpret_cast<int2 *>(ws + L.tile_info);
+    int32_t *tile_order = reinterpret_cast<int32_t *>(ws + L.tile_order);
     int32_t *sorted_ids = reinterpret_cast<int32_t *>(ws + L.sorted_ids);
     uint16_t *h = reinterpret_cast<uint16_t *>(ws + L.h);
     uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
 
     gu.sorted_ids = dn.sorted_ids = sorted_ids;
     gu.tile_info = dn.tile_info = tile_info;
+    if (chunks)
+        gu.tile_order = dn.tile_order = tile_order;
     gu.a_src = x;
     gu.q = gu_q;
     gu.s = gu_s;
@@ -325,7 +330,7 @@ int moe_forward_impl(const uint16_t *x, const int32_t *topk_ids, const float *to
     } else {
         if ((err = dgw4::launch_align(topk_ids, (int)A, E, block_m, (long long)cap, counts,
                                       offsets, sorted_ids, tile_expert, num_padded, tile_info,
-                                      st)) != hipSuccess ||
+                                      chunks ? tile_order : nullptr, st)) != hipSuccess ||
             (err = mark(1)) != hipSuccess)
             return from_hip(err);
         if ((err = chunks ? dgw4::launch_chunk_gate_up(gu, st) : dgw4::launch_gate_up(gu, gu_g, st)) !=

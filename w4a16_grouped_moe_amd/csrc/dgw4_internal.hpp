@@ -37,11 +37,13 @@ __host__ __device__ constexpr int tile_count(int y) { return y >> 16; }
 // Alignment of the flat assignment ids to experts (one workgroup per
 // expert). tile_info may be null; otherwise tile_info[j] = {expert, rows of
 // the tile that hold assignments | tiles of the expert << 16} for live tiles,
-// {-1, 0} past the total.
+// {-1, 0} past the total. order may be null; otherwise order[k] = the tile
+// with the k-th most rows (ties to the lower tile index) for k below the
+// tile total, -1 past it: the order in which the chunk GEMMs take tiles.
 hipError_t launch_align(const int32_t *topk_ids, int A, int E, int block_m, long long cap,
                         int32_t *counts, int32_t *offsets, int32_t *sorted_ids,
                         int32_t *tile_expert, int32_t *num_padded, int2 *tile_info,
-                        hipStream_t stream);
+                        int32_t *order, hipStream_t stream);
 
 // Router: ids int32 [T, topk] (the topk largest logits, largest first, ties
 // to the lower id) and w fp32 [T, topk] (softmax over the chosen logits) from
@@ -63,6 +65,7 @@ struct GemmArgs {
     int a_rows;                 // rows of a_src (T or cap)
     const int32_t *sorted_ids;  // [cap]
     const int2 *tile_info;      // [cap / kBlockM]: {expert or -1, valid rows}
+    const int32_t *tile_order;  // chunk GEMMs: [max_tiles] tiles, most rows first (-1 past the total)
     const uint8_t *q;           // packed weights [E, n_w, K/2], canonical or tiled (see tiled)
     const uint16_t *s;          // [E, n_w, K/g]
     const uint16_t *z;          // [E, n_w, K/g]

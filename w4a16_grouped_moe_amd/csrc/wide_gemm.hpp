@@ -158,13 +158,17 @@ __device__ __forceinline__ WideBlock wide_block(const GemmArgs &p, int NG)
         b.wrow = b.col0 + lcol;
         b.nmb = kLwRows / 16;
     } else {
-        // workgroup -> (chunk, column block): the column blocks of a chunk
-        // run on one XCD, back to back, so its activation rows stay in that
-        // XCD's L2
+        // workgroup -> (k-th chunk in the alignment's order, most rows
+        // first, column block): the column blocks of a chunk run on one XCD,
+        // back to back, so its activation rows stay in that XCD's L2; the
+        // longest chunks start first, so the last round holds short ones
         constexpr int kBlockCols = MODE == kModeGateUp ? wide_cols<MODE>() / 2 : wide_cols<MODE>();
         const int ncb = (p.n_out + kBlockCols - 1) / kBlockCols;
-        const int chunk = slot / ncb * kXcds + xcd;
-        if (chunk >= p.max_tiles)
+        const int k = slot / ncb * kXcds + xcd;
+        if (k >= p.max_tiles)
+            return b;
+        const int chunk = p.tile_order ? p.tile_order[k] : k;
+        if (chunk < 0 || chunk >= p.max_tiles)
             return b;
         const int2 ti = p.tile_info[chunk];
         if (ti.x < 0)
