@@ -840,27 +840,48 @@ __device__ int layer_tile_find(const int32_t *__restrict__ ids, int A, int E, in
                 atomicAdd(&s_cnt[v[j]], 1);
     }
     __syncthreads();
-    // padded offsets in expert order, one expert per thread (E <=
-    // kL4Threads, see layer_fused); the tile follows from the total (see
-    // layer_tile_of), and the thread whose expert's rows hold the tile's
+    // padded offsets in expert order, all in wave 0 (E <= kL4Threads, see
+    // layer_fused: kEPer consecutive experts per lane, then a wave scan, so
+    // one barrier publishes the result); the tile follows from the total
+    // (see layer_tile_of), and the lane whose expert's rows hold the tile's
     // first row records it
-    const int cnt = tid < E ? s_cnt[tid] : 0;
-    const int padded = (cnt + kBlockM - 1) / kBlockM * kBlockM;
-    int total;
-    const int off = l4_scan_excl(padded, s_wsum, total);
-    const int tile = layer_tile_of(xcd, tslot, total);
-    const int row = tile < 0 ? INT_MAX : tile * kBlockM;
-    if (tid < E && off <= row && row < off + padded) {
-        s_info[0] = tid;
-        s_info[1] = off;
-        s_info[2] = cnt;
-        s_info[3] = padded / kBlockM;
+    if (tid < 64) {
+        constexpr int kEPer = (kL4Threads + 63) / 64;
+        int c[kEPer], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kEPer; ++j) {
+            const int x = tid * kEPer + j;
+            c[j] = x < E ? s_cnt[x] : 0;
+            sum += (c[j] + kBlockM - 1) / kBlockM * kBlockM;
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d, 64);
+            if (tid >= d)
+                incl += u;
+        }
+        const int total = __shfl(incl, 63, 64);
+        const int tile = layer_tile_of(xcd, tslot, total);
+        const int row = tile < 0 ? INT_MAX : tile * kBlockM;
+        int off = incl - sum;
+#pragma unroll
+        for (int j = 0; j < kEPer; ++j) {
+            const int padded = (c[j] + kBlockM - 1) / kBlockM * kBlockM;
+            if (off <= row && row < off + padded) {
+                s_info[0] = tid * kEPer + j;
+                s_info[1] = row - off;                 // the tile's first rank within the expert
+                s_info[2] = c[j];
+                s_info[3] = padded / kBlockM;
+            }
+            off += padded;
+        }
     }
     __syncthreads();
     // uniform over the workgroup: scalar registers
     const int e = __builtin_amdgcn_readfirstlane(s_info[0]);
     if (e >= 0) {
-        ts.r0 = __builtin_amdgcn_readfirstlane(row - s_info[1]);
+        ts.r0 = __builtin_amdgcn_readfirstlane(s_info[1]);
         ts.valid = __builtin_amdgcn_readfirstlane(min(kBlockM, s_info[2] - ts.r0));
         ts.tiles = __builtin_amdgcn_readfirstlane(s_info[3]);
     }
