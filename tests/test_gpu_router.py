@@ -42,6 +42,16 @@ def test_router_matches_oracle(T, E, topk):
     lg[:, ::3] = np.round(lg[:, ::3], 1)                  # exact ties
     if T > 2:
         lg[2, :] = 0.5                                     # a row of equal logits
+    if T > 4:
+        # +0 and -0 compare equal (ties to the lower id); negative values,
+        # subnormals and the extremes of the fp32 range order as floats
+        lg[3, :] = np.where(np.arange(E) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+        lg[3, ::5] = -1.0
+        lg[4, :] = -np.abs(lg[4, :])
+        lg[4, 1::4] = np.float32(1e-40)
+        lg[4, 2::4] = np.float32(-1e-40)
+        lg[4, 3::7] = np.float32(-3.4e38)
+        lg[4, 0] = np.float32(3.4e38)
     _check(lg, topk, f"T={T} E={E} top-{topk}")
 
 

@@ -15,8 +15,12 @@
 // One wave per token, no sequential rounds: the token's logits go to a slot
 // of LDS, every lane ranks the logits it holds against all of them (rank =
 // how many logits are larger, or equal at a lower id), and the logit of rank
-// k < topk is choice k. The weights' exp terms are laid out in choice order
-// and summed in that order by every lane.
+// k < topk is choice k. Each comparison is one unsigned 64-bit compare of
+// keys (the logit's bits mapped to an order-preserving unsigned integer,
+// -0 as +0, above the complement of the id), which orders exactly as
+// "larger logit, or equal logit at a lower id" for finite logits. The
+// weights' exp terms are laid out in choice order and summed in that order
+// by every lane.
 #include "dgw4_internal.hpp"
 
 #include <cmath>
@@ -26,11 +30,17 @@ namespace {
 
 constexpr int kRouterWaves = 4;                  // tokens per workgroup
 
-// (v, e) ranks before (v2, e2): the larger value, or the same value at a
-// smaller id
-__device__ inline bool before(float v, int e, float v2, int e2)
+// The ranking key of logit v of expert e: a larger key ranks first. The
+// float's bits become an unsigned integer in the floats' order (negative
+// values complemented, non-negative ones with the top bit set; -0 as +0),
+// the id's complement below it puts equal logits in ascending id order.
+__device__ inline uint64_t rank_key(float v, int e)
 {
-    return v > v2 || (v == v2 && e < e2);
+    uint32_t b = __builtin_bit_cast(uint32_t, v);
+    if (b == 0x80000000u)
+        b = 0u;
+    const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (uint64_t)u << 32 | (uint32_t)~e;
 }
 
 template <int PER>
@@ -39,7 +49,7 @@ __global__ void __launch_bounds__(kRouterWaves * 64) router_kernel(const float *
                                                                   int32_t *__restrict__ ids,
                                                                   float *__restrict__ w)
 {
-    __shared__ float s_l[kRouterWaves][PER * 64];    // the token's logits
+    __shared__ uint64_t s_k[kRouterWaves][PER * 64]; // the token's ranking keys
     __shared__ float s_x[kRouterWaves][64];          // exp terms in choice order
     __shared__ float s_v[kRouterWaves][64];          // chosen logits in choice order
     const int lane = threadIdx.x & 63;
@@ -49,12 +59,14 @@ __global__ void __launch_bounds__(kRouterWaves * 64) router_kernel(const float *
         return;                                      // whole waves: no barrier below
     const float *l = logits + (size_t)t * E;
     float v[PER];
+    uint64_t key[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int e = lane + 64 * j;
         v[j] = e < E ? l[e] : 0.0f;
+        key[j] = rank_key(v[j], e);
         if (e < E)
-            s_l[wv][e] = v[j];
+            s_k[wv][e] = key[j];
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -63,10 +75,10 @@ __global__ void __launch_bounds__(kRouterWaves * 64) router_kernel(const float *
     for (int j = 0; j < PER; ++j)
         rank[j] = 0;
     for (int e2 = 0; e2 < E; ++e2) {                 // the same address for all lanes: a broadcast
-        const float v2 = s_l[wv][e2];
+        const uint64_t k2 = s_k[wv][e2];
 #pragma unroll
         for (int j = 0; j < PER; ++j)
-            rank[j] += before(v2, e2, v[j], lane + 64 * j);
+            rank[j] += k2 > key[j];
     }
     // choice k: its id, its logit; the largest logit is choice 0
 #pragma unroll
