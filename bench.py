@@ -656,6 +656,7 @@ def main() -> int:
     probe["pct_of_probe"] = round(100 * gbps / probe["gbps"], 2)
     traffic = measured_traffic(traffic_key(shape, args.weight_layout, row_block))
     pages_gbps = layers[0]["bytes"]["layer"] / (GB10_LAYER_MS * 1e-3) / 1e9
+    kern_flops = 2 * shape.T * shape.topk * (2 * shape.m * shape.d + shape.d * shape.m)
     result = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -718,6 +719,16 @@ def main() -> int:
                             f"of the expert stages (dgw4_moe_experts) over the rotated layers"),
             "bytes_source": ("packed q + s + z of the populated experts plus x, per launch; "
                              "H, Y and alignment workspace traffic not counted"),
+        },
+        # the same launches against the fp16 MFMA peak: every assignment row
+        # through gate_up (2m x d) and down (d x m), padding rows not counted
+        "mfma": {
+            "achieved": round(kern_flops / (kern_us * 1e-6) / 1e12, 1),
+            "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kern_flops / (kern_us * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "flops_per_launch": kern_flops,
+            "note": "MfmaUtil per kernel (rocprofv3) is in profiles/expert_stages_workloads_utilisation_stack_skew_wide.md",
         },
     }
     if not args.no_cpu_baseline:
