@@ -243,6 +243,12 @@ DGW4_API int dgw4_router(const float *logits, int T, int E, int topk, int32_t *i
  *              irrelevant; the call overwrites what it uses.
  *   ws_bytes   host pointer: in = size of workspace, out (query) = required
  *   out        device fp16 bits [T, d]                   (output)
+ * The kernels address x, the gated intermediate (T * topk + E * 31 padded
+ * rows x m fp16 on 32-row tiles), the expert outputs and one expert's
+ * packed weights through 32-bit byte offsets: a call where any of them
+ * would reach 2 GiB returns DGW4_ERR_UNSUPPORTED (the query too), and
+ * 128-row chunks are only taken where T * topk * d * 2 < 2 GiB. At d = 2816,
+ * m = 704, E = 128, top-8 that is T <= 190154 (T <= 47662 on chunks).
  */
 DGW4_API int dgw4_moe_forward(const uint16_t *x, const int32_t *topk_ids, const float *topk_w,
                      int T, int topk, int E, int d, int m,
